@@ -1,0 +1,211 @@
+/*
+ * st.h -- C ABI of the ST-DiT attention block on AMD MI355X (gfx950).
+ *
+ * The block, as the pages state it:
+ *   - ScaleFusion review, "Technical architecture": an ST-DiT alternates a
+ *     spatial layer (attention over the S patch tokens of each frame, input
+ *     [B, T, S, C]) and a temporal layer (attention over the T frames of each
+ *     patch); between them the tensor is redistributed between the
+ *     [B, T, S, C] and [B, S, T, C] orders (an all-to-all across GPUs, a local
+ *     permutation on one GPU).  Spatial-temporal independence: slicing along T
+ *     commutes with the spatial layer, slicing along S with the temporal layer.
+ *   - ScaleFusion review, "Core innovations", algorithm pseudocode: the input is
+ *     rearranged to [B, N_T, N_S, T/N_T, S/N_S, C] and each layer runs slice by
+ *     slice; the output returns to [B, T, S, C].
+ *   - CoCoDiff page, "V-First compute scheduling": Q, K, V come from a linear
+ *     projection; Q and K then get RMSNorm and RoPE, V gets neither.
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is a DEVICE pointer owned by the caller, unless the
+ *     comment says "host".  The library never allocates, frees, or keeps state
+ *     between calls.  Scratch space, where needed, is a caller-provided
+ *     workspace whose size the matching *_workspace() query returns.
+ *   - dtype: ST_BF16 (bf16 storage, fp32 arithmetic and accumulation, outputs
+ *     rounded to nearest-even) or ST_F32 (fp32 storage and arithmetic).
+ *     RMSNorm gains and RoPE tables are always fp32.
+ *   - Row-major layouts; the last listed dimension is contiguous.
+ *   - Weights are "out-features major": w_qkv [3*H*d, c_in], w_o [c_out, H*d];
+ *     y = x . w^T.  Rows 0..H*d-1 of w_qkv produce q (channel h*d + j), the
+ *     next H*d produce k, the last H*d produce v.
+ *   - stream is a hipStream_t (NULL: the default stream).  Calls validate
+ *     their arguments on the host, enqueue kernels on the stream and return;
+ *     they never synchronise.  Device faults surface at the caller's sync.
+ *   - Errors are return codes only.  Argument validation happens before any
+ *     HIP call, so an invalid call has no side effect.  Outputs must not alias
+ *     inputs (ST_EINVAL).  Pointers must be 16-byte aligned (ST_EALIGN) except
+ *     for st_relayout, which needs element alignment only.
+ *   - Calls are reentrant; concurrent calls on different streams are safe as
+ *     long as their output buffers and workspaces do not overlap.
+ */
+#ifndef ST_H
+#define ST_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ST_OK = 0,
+  ST_EINVAL = 1,        /* bad shape, NULL pointer, aliasing, unknown enum     */
+  ST_EUNSUPPORTED = 2,  /* valid request this build has no kernel for          */
+  ST_EALIGN = 3,        /* pointer not aligned as required                     */
+  ST_EWORKSPACE = 4,    /* workspace NULL or smaller than the query returned   */
+  ST_ELAUNCH = 5        /* a HIP launch reported an error                      */
+} st_status;
+
+typedef enum { ST_F32 = 0, ST_BF16 = 1 } st_dtype;
+
+typedef enum {
+  ST_ROPE_NONE = 0,     /* no rotation                                         */
+  ST_ROPE_1D = 1,       /* one segment over all d channels, position p = t     */
+  ST_ROPE_2D = 2        /* axial: channels [0, d/2) by patch row h,
+                           [d/2, d) by patch column w                          */
+} st_rope_kind;
+
+/* Human-readable name of a status code (static string). */
+const char *st_status_str(int status);
+
+/*
+ * st_rope_table -- cosine/sine table of the rotary position encoding.
+ * CoCoDiff page, "V-First compute scheduling" (RoPE on Q and K).  The rotation
+ * of channel pair (2i, 2i+1) inside an axis segment of length m is
+ * theta = p * base^(-2i/m): m = d for ST_ROPE_1D, m = d/2 for ST_ROPE_2D.
+ *
+ *   table  out  fp32 [n_pos][m/2][2] = (cos theta, sin theta) for p = 0..n_pos-1,
+ *               computed in double precision on the device, rounded to fp32.
+ *               Holds st_rope_table_floats(d, kind, n_pos) floats.
+ * Errors: ST_EINVAL if kind is not 1D/2D, d is not even (1D) or not a multiple
+ * of 4 (2D), n_pos < 1, base <= 0, table NULL.
+ */
+size_t st_rope_table_floats(int d, int kind, int n_pos);
+st_status st_rope_table(int d, int kind, float base, int n_pos, float *table, void *stream);
+
+/*
+ * st_qkv_norm_rope -- QKV projection, then per-head RMSNorm and RoPE on q and k.
+ * CoCoDiff page, "V-First compute scheduling": projection -> RMSNorm -> RoPE
+ * for Q and K; V is the projection only.
+ *
+ *   x        in   [rows, c_in]           (dtype)
+ *   w_qkv    in   [3*H*d, c_in]          (dtype)
+ *   g_q,g_k  in   fp32 [d]               RMSNorm gains, shared by the heads
+ *   eps           RMSNorm epsilon: t_j * g_j / sqrt(mean_j t_j^2 + eps), per (row, head)
+ *   rope_kind     st_rope_kind.  ST_ROPE_NONE ignores the four arguments below.
+ *   rope_table in fp32 table from st_rope_table() for the same d and kind
+ *   rope_npos     positions in the table; every position used must be < rope_npos
+ *   pos_period, pos_offset, grid_w
+ *                 position of row r: i = r % pos_period + pos_offset;
+ *                 1D: p = i;  2D: h = i / grid_w, w = i % grid_w.
+ *                 Rows in [.., S] order with pos_period = S give a frame's
+ *                 patches; rows in [.., T] order with pos_period = T give frames.
+ *   H, d          heads and head dim; dtype ST_BF16 supports d in {64, 72, 128},
+ *                 ST_F32 supports even d <= 128 (multiple of 4 for 2D RoPE).
+ *   q, k, v  out  [rows, H, d]           (dtype)
+ * c_in must be a multiple of 8.  rows may be 0 (no work).
+ */
+st_status st_qkv_norm_rope(const void *x, int64_t rows, int c_in, const void *w_qkv,
+                           const float *g_q, const float *g_k, float eps,
+                           int rope_kind, const float *rope_table, int rope_npos,
+                           int64_t pos_period, int64_t pos_offset, int grid_w,
+                           int H, int d, int dtype, void *q, void *k, void *v, void *stream);
+
+/*
+ * st_out_proj -- output projection of the attention result: y = a . w^T.
+ * The pages do not spell the layer's output projection out; the layer is read
+ * as projection -> norm/RoPE -> attention -> output projection.
+ *
+ *   a  in  [rows, k_in]   w in [n_out, k_in]   y out [rows, n_out]   (dtype)
+ * k_in must be a multiple of 8, n_out a multiple of 4.
+ */
+st_status st_out_proj(const void *a, int64_t rows, int k_in, const void *w, int n_out,
+                      int dtype, void *y, void *stream);
+
+/*
+ * st_attn_spatial -- spatial attention: for every (b, t, h),
+ *   O = softmax(Q K^T * scale) V over the S patch tokens of frame t.
+ * ScaleFusion review, "Technical architecture" (the spatial layer attends over
+ * S); the cost is quadratic in S (PipeFusion summary, "Problem definition").
+ *
+ *   q, k, v  in   [B, T, S, H, d]   (the [rows, H, d] output of st_qkv_norm_rope
+ *                                     for rows in [B, T, S] order)
+ *   out      out  [B, T, S, H, d]
+ *   scale         usually 1/sqrt(d); passed by the caller
+ * Same d support as st_qkv_norm_rope.  S >= 1.
+ */
+st_status st_attn_spatial(const void *q, const void *k, const void *v, int B, int T, int S,
+                          int H, int d, float scale, int dtype, void *out, void *stream);
+
+/*
+ * st_attn_temporal -- temporal attention: for every (b, s, h),
+ *   O = softmax(Q K^T * scale) V over the T frames of patch s,
+ * where keys at frames t >= t_valid get weight exactly 0 (frames appended to
+ * make T a multiple of the slice count N_T; their query rows are computed
+ * but carry no meaning).
+ * ScaleFusion review, "Technical architecture" (the temporal layer attends over T).
+ *
+ *   q, k, v  in   [B, S, T, H, d]
+ *   out      out  [B, S, T, H, d]
+ *   1 <= t_valid <= T.
+ */
+st_status st_attn_temporal(const void *q, const void *k, const void *v, int B, int S, int T,
+                           int t_valid, int H, int d, float scale, int dtype, void *out,
+                           void *stream);
+
+/*
+ * st_relayout -- strided N-D copy, the one-GPU form of the spatial <-> temporal
+ * redistribution (ScaleFusion review, "Technical architecture", execution flow)
+ * and of the blocked rearranges and slice gathers/scatters of the algorithm
+ * pseudocode ("Core innovations").
+ *
+ * For every multi-index i with 0 <= i_k < dims[k]:
+ *     dst[sum_k i_k * dst_strides[k]] = src[sum_k i_k * src_strides[k]]
+ * dims, src_strides, dst_strides are HOST arrays of ndim int64 values;
+ * strides are in elements.  1 <= ndim <= 6, elem_bytes in {1, 2, 4, 8, 16}.
+ * The destination index map must be one-to-one and must not overlap the
+ * source (not checked beyond src != dst).  Bit-exact copy.
+ */
+st_status st_relayout(const void *src, const int64_t *src_strides, void *dst,
+                      const int64_t *dst_strides, const int64_t *dims, int ndim,
+                      int elem_bytes, void *stream);
+
+/* Weights of one layer (all device pointers). */
+typedef struct {
+  const void *w_qkv;   /* [3*H*d, C] */
+  const void *w_o;     /* [C, H*d]   */
+  const float *g_q;    /* [d] */
+  const float *g_k;    /* [d] */
+} st_layer_weights;
+
+/*
+ * st_block_sliced -- the spatial + temporal layer pair under the slicing
+ * schedule at one GPU (ScaleFusion review, "Core innovations": intra-layer
+ * scheduling and the algorithm pseudocode; N_T = N_S = 4 in "Experimental
+ * results").  x [B, T, S, C] is rearranged to [B, N_T, N_S, T/N_T, S/N_S, C];
+ * the spatial layer runs once per time slice (T/N_T frames, all S patches,
+ * 2D RoPE with global (h, w)), the temporal layer once per space slice
+ * (S/N_S patches, all T frames, 1D RoPE with global t, keys t >= t_valid
+ * masked); the result is rearranged back to y [B, T, S, C].
+ * n_t = n_s = 1 is the unsliced layer pair.
+ *
+ *   x         in   [B, T, S, C]   T % n_t == 0, S % n_s == 0 (the caller pads T
+ *                                 with zero frames and passes t_valid)
+ *   grid_w         patch-grid width; S % grid_w == 0; s = h * grid_w + w
+ *   spatial, temporal   host pointers to the two layers' weights
+ *   y         out  [B, T, S, C]
+ *   ws             device workspace of at least st_block_sliced_workspace() bytes
+ * Each output element is computed by the same arithmetic in the same order
+ * whatever n_t and n_s are, so sliced and unsliced results are bit-identical.
+ */
+st_status st_block_sliced(const void *x, int B, int T, int t_valid, int S, int grid_w, int C,
+                          int H, int d, int n_t, int n_s, const st_layer_weights *spatial,
+                          const st_layer_weights *temporal, float eps, float rope_base,
+                          int dtype, void *y, void *ws, size_t ws_bytes, void *stream);
+size_t st_block_sliced_workspace(int B, int T, int S, int grid_w, int C, int H, int d,
+                                 int n_t, int n_s, int dtype);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ST_H */

@@ -1,0 +1,360 @@
+// C ABI of libst.so: argument validation (host only, before any HIP call),
+// dispatch to the bf16 MFMA or fp32 kernels, and the layer-pair orchestration
+// of st_block_sliced (ScaleFusion review, "Core innovations": intra-layer
+// scheduling and algorithm pseudocode, at one GPU).
+#include <math.h>
+
+#include <algorithm>
+
+#include "st_internal.h"
+
+using namespace st;
+
+namespace {
+
+inline size_t esize(int dt) { return dt == ST_BF16 ? 2 : 4; }
+inline bool dtype_ok(int dt) { return dt == ST_BF16 || dt == ST_F32; }
+
+struct Range {
+  uintptr_t lo, hi;
+};
+inline Range rng(const void *p, int64_t bytes) { return Range{(uintptr_t)p, (uintptr_t)p + (uintptr_t)bytes}; }
+inline bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+
+bool head_dim_ok(int d, int dt, int rope_kind) {
+  if (d < 2 || d > 128 || d % 2) return false;
+  if (rope_kind == ST_ROPE_2D && d % 4) return false;
+  if (dt == ST_BF16) return attn_bf16_supported(d);
+  return true;
+}
+
+st_status check_rope(int kind, const float *table, int npos, int64_t period, int64_t offset, int grid_w, int d,
+                     int64_t rows) {
+  if (kind == ST_ROPE_NONE) return ST_OK;
+  if (kind != ST_ROPE_1D && kind != ST_ROPE_2D) return ST_EINVAL;
+  if (!table || npos < 1 || period < 1 || offset < 0) return ST_EINVAL;
+  if (!aligned16(table)) return ST_EALIGN;
+  const int64_t imax = std::min<int64_t>(period, std::max<int64_t>(rows, 1)) - 1 + offset;   // largest index used
+  if (kind == ST_ROPE_1D) return imax < npos ? ST_OK : ST_EINVAL;
+  if (grid_w < 1 || d % 4) return ST_EINVAL;
+  if (imax / grid_w >= npos || std::min<int64_t>(grid_w - 1, imax) >= npos) return ST_EINVAL;
+  return ST_OK;
+}
+
+// ---------------------------------------------------------------- dispatch
+st_status do_qkv(const void *x, int64_t rows, int c_in, const void *w, const float *gq, const float *gk, float eps,
+                 const RopeArgs &rope, int H, int d, int dt, void *q, void *k, void *v, hipStream_t s) {
+  if (dt == ST_BF16) return launch_qkv_bf16(x, rows, c_in, w, gq, gk, eps, rope, H, d, q, k, v, s);
+  return launch_qkv_f32((const float *)x, rows, c_in, (const float *)w, gq, gk, eps, rope, H, d, (float *)q,
+                        (float *)k, (float *)v, s);
+}
+
+st_status do_linear(const void *a, int64_t rows, int k_in, const void *w, int n_out, int dt, void *y, hipStream_t s) {
+  if (dt == ST_BF16) return launch_linear_bf16(a, rows, k_in, w, n_out, y, s);
+  return launch_linear_f32((const float *)a, rows, k_in, (const float *)w, n_out, (float *)y, s);
+}
+
+st_status do_attn(const void *q, const void *k, const void *v, int64_t outer, int L, int nv, int H, int d, float scale,
+                  int dt, void *out, bool short_ok, hipStream_t s) {
+  if (dt == ST_F32)
+    return launch_attn_f32((const float *)q, (const float *)k, (const float *)v, outer, L, nv, H, d, scale,
+                           (float *)out, s);
+  if (short_ok && attn_short_supported(L, d)) return launch_attn_short_bf16(q, k, v, outer, L, nv, H, d, scale, out, s);
+  return launch_attn_bf16(q, k, v, outer, L, nv, H, d, scale, out, s);
+}
+
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+struct BlockPlan {
+  size_t rope2, rope1, xb, hb, xs, q, k, v, o, ys, total;
+  int npos2, npos1;
+};
+
+BlockPlan plan_block(int B, int T, int S, int grid_w, int C, int H, int d, int n_t, int n_s, int dt) {
+  BlockPlan p{};
+  const size_t e = esize(dt);
+  const int64_t N = (int64_t)B * T * S;
+  const int64_t hd = (int64_t)H * d;
+  p.npos2 = std::max(S / grid_w, grid_w);
+  p.npos1 = T;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align256(bytes);
+    return at;
+  };
+  p.rope2 = take((size_t)p.npos2 * (d / 4) * 2 * sizeof(float));
+  p.rope1 = take((size_t)p.npos1 * (d / 2) * 2 * sizeof(float));
+  const bool sliced = n_t > 1 || n_s > 1;
+  int64_t rows;
+  if (sliced) {
+    p.xb = take(N * C * e);
+    p.hb = take(N * C * e);
+    rows = std::max<int64_t>((int64_t)B * (T / n_t) * S, (int64_t)B * (S / n_s) * T);
+    p.xs = take(rows * C * e);
+  } else {
+    p.hb = take(N * C * e);   // spatial output [B,T,S,C], later the temporal output [B,S,T,C]
+    p.xs = take(N * C * e);   // [B,S,T,C] input of the temporal layer
+    rows = N;
+  }
+  p.q = take(rows * hd * e);
+  p.k = take(rows * hd * e);
+  p.v = take(rows * hd * e);
+  p.o = take(rows * hd * e);
+  p.ys = sliced ? take(rows * C * e) : 0;
+  p.total = off;
+  return p;
+}
+
+// One layer: projection + norm/RoPE, attention, output projection.
+st_status run_layer(const void *x, int64_t outer, int L, int nv, int C, int H, int d, const st_layer_weights *w,
+                    float eps, const RopeArgs &rope, int dt, void *q, void *k, void *v, void *o, void *y,
+                    bool temporal, hipStream_t s) {
+  const int64_t rows = outer * L;
+  st_status r = do_qkv(x, rows, C, w->w_qkv, w->g_q, w->g_k, eps, rope, H, d, dt, q, k, v, s);
+  if (r != ST_OK) return r;
+  r = do_attn(q, k, v, outer, L, nv, H, d, (float)(1.0 / sqrt((double)d)), dt, o, temporal, s);
+  if (r != ST_OK) return r;
+  return do_linear(o, rows, H * d, w->w_o, C, dt, y, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *st_status_str(int status) {
+  switch (status) {
+    case ST_OK: return "ok";
+    case ST_EINVAL: return "invalid argument";
+    case ST_EUNSUPPORTED: return "unsupported";
+    case ST_EALIGN: return "misaligned pointer";
+    case ST_EWORKSPACE: return "workspace too small";
+    case ST_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t st_rope_table_floats(int d, int kind, int n_pos) {
+  if (n_pos < 1 || d < 2) return 0;
+  if (kind == ST_ROPE_1D) return (size_t)n_pos * (d / 2) * 2;
+  if (kind == ST_ROPE_2D) return (size_t)n_pos * (d / 4) * 2;
+  return 0;
+}
+
+st_status st_rope_table(int d, int kind, float base, int n_pos, float *table, void *stream) {
+  if (kind != ST_ROPE_1D && kind != ST_ROPE_2D) return ST_EINVAL;
+  if (d < 2 || d > 4096 || d % 2 || (kind == ST_ROPE_2D && d % 4)) return ST_EINVAL;
+  if (n_pos < 1 || !(base > 0.f) || !isfinite(base) || !table) return ST_EINVAL;
+  if (!aligned16(table)) return ST_EALIGN;
+  if ((int64_t)n_pos * d >= (1ll << 31)) return ST_EUNSUPPORTED;
+  return launch_rope_table(d, kind, (double)base, n_pos, table, (hipStream_t)stream);
+}
+
+st_status st_qkv_norm_rope(const void *x, int64_t rows, int c_in, const void *w_qkv, const float *g_q,
+                           const float *g_k, float eps, int rope_kind, const float *rope_table, int rope_npos,
+                           int64_t pos_period, int64_t pos_offset, int grid_w, int H, int d, int dtype, void *q,
+                           void *k, void *v, void *stream) {
+  if (!dtype_ok(dtype)) return ST_EINVAL;
+  if (!x || !w_qkv || !g_q || !g_k || !q || !k || !v) return ST_EINVAL;
+  if (rows < 0 || c_in < 1 || H < 1 || !(eps >= 0.f) || !isfinite(eps)) return ST_EINVAL;
+  if (rope_kind != ST_ROPE_NONE && rope_kind != ST_ROPE_1D && rope_kind != ST_ROPE_2D) return ST_EINVAL;
+  if (d < 2 || d % 2 || (rope_kind == ST_ROPE_2D && d % 4)) return ST_EINVAL;
+  if (!head_dim_ok(d, dtype, rope_kind)) return ST_EUNSUPPORTED;
+  if (dtype == ST_BF16 && c_in % 8) return ST_EUNSUPPORTED;
+  const st_status rs = check_rope(rope_kind, rope_table, rope_npos, pos_period, pos_offset, grid_w, d, rows);
+  if (rs != ST_OK) return rs;
+  if ((int64_t)H * d * 3 >= (1 << 30) || rows >= (1ll << 40)) return ST_EUNSUPPORTED;
+  for (const void *p : {x, w_qkv, (const void *)g_q, (const void *)g_k, (const void *)q, (const void *)k,
+                        (const void *)v})
+    if (!aligned16(p)) return ST_EALIGN;
+  const size_t e = esize(dtype);
+  const Range rx = rng(x, rows * c_in * e), rw = rng(w_qkv, (int64_t)3 * H * d * c_in * e);
+  const Range rq = rng(q, rows * H * d * e), rk = rng(k, rows * H * d * e), rv = rng(v, rows * H * d * e);
+  for (Range out : {rq, rk, rv})
+    if (overlap(out, rx) || overlap(out, rw)) return ST_EINVAL;
+  if (overlap(rq, rk) || overlap(rq, rv) || overlap(rk, rv)) return ST_EINVAL;
+  RopeArgs ra{rope_kind, rope_npos, rope_table, pos_period, pos_offset, grid_w};
+  return do_qkv(x, rows, c_in, w_qkv, g_q, g_k, eps, ra, H, d, dtype, q, k, v, (hipStream_t)stream);
+}
+
+st_status st_out_proj(const void *a, int64_t rows, int k_in, const void *w, int n_out, int dtype, void *y,
+                      void *stream) {
+  if (!dtype_ok(dtype)) return ST_EINVAL;
+  if (!a || !w || !y || rows < 0 || k_in < 1 || n_out < 1) return ST_EINVAL;
+  if (n_out % 4 || (dtype == ST_BF16 && k_in % 8)) return ST_EUNSUPPORTED;
+  if (rows >= (1ll << 40) || (int64_t)k_in * n_out >= (1ll << 40)) return ST_EUNSUPPORTED;
+  if (!aligned16(a) || !aligned16(w) || !aligned16(y)) return ST_EALIGN;
+  const size_t e = esize(dtype);
+  const Range ry = rng(y, rows * n_out * e);
+  if (overlap(ry, rng(a, rows * k_in * e)) || overlap(ry, rng(w, (int64_t)n_out * k_in * e))) return ST_EINVAL;
+  return do_linear(a, rows, k_in, w, n_out, dtype, y, (hipStream_t)stream);
+}
+
+static st_status attn_common(const void *q, const void *k, const void *v, int64_t outer, int L, int nv, int H, int d,
+                             float scale, int dtype, void *out, bool temporal, void *stream) {
+  if (!dtype_ok(dtype)) return ST_EINVAL;
+  if (!q || !k || !v || !out || H < 1 || d < 2 || d % 2) return ST_EINVAL;
+  if (!(scale > 0.f) || !isfinite(scale)) return ST_EINVAL;
+  if (!head_dim_ok(d, dtype, ST_ROPE_NONE)) return ST_EUNSUPPORTED;
+  if (outer >= (1ll << 40) || L >= (1 << 30)) return ST_EUNSUPPORTED;
+  for (const void *p : {q, k, v, (const void *)out})
+    if (!aligned16(p)) return ST_EALIGN;
+  const int64_t bytes = outer * L * H * d * (int64_t)esize(dtype);
+  const Range ro = rng(out, bytes);
+  if (overlap(ro, rng(q, bytes)) || overlap(ro, rng(k, bytes)) || overlap(ro, rng(v, bytes))) return ST_EINVAL;
+  return do_attn(q, k, v, outer, L, nv, H, d, scale, dtype, out, temporal, (hipStream_t)stream);
+}
+
+st_status st_attn_spatial(const void *q, const void *k, const void *v, int B, int T, int S, int H, int d, float scale,
+                          int dtype, void *out, void *stream) {
+  if (B < 0 || T < 0 || S < 0) return ST_EINVAL;
+  return attn_common(q, k, v, (int64_t)B * T, S, S, H, d, scale, dtype, out, false, stream);
+}
+
+st_status st_attn_temporal(const void *q, const void *k, const void *v, int B, int S, int T, int t_valid, int H, int d,
+                           float scale, int dtype, void *out, void *stream) {
+  if (B < 0 || S < 0 || T < 0) return ST_EINVAL;
+  if (T > 0 && (t_valid < 1 || t_valid > T)) return ST_EINVAL;
+  return attn_common(q, k, v, (int64_t)B * S, T, t_valid, H, d, scale, dtype, out, true, stream);
+}
+
+st_status st_relayout(const void *src, const int64_t *src_strides, void *dst, const int64_t *dst_strides,
+                      const int64_t *dims, int ndim, int elem_bytes, void *stream) {
+  if (!src || !dst || !src_strides || !dst_strides || !dims) return ST_EINVAL;
+  if (ndim < 1 || ndim > 6) return ST_EINVAL;
+  if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8 && elem_bytes != 16) return ST_EINVAL;
+  if (src == dst) return ST_EINVAL;
+  int64_t smin = 0, smax = 0, dmin = 0, dmax = 0;
+  bool empty = false;
+  for (int i = 0; i < ndim; ++i) {
+    if (dims[i] < 0) return ST_EINVAL;
+    if (dims[i] == 0) empty = true;
+    const int64_t ext = dims[i] > 0 ? dims[i] - 1 : 0;
+    (src_strides[i] >= 0 ? smax : smin) += src_strides[i] * ext;
+    (dst_strides[i] >= 0 ? dmax : dmin) += dst_strides[i] * ext;
+  }
+  if ((uintptr_t)src % elem_bytes || (uintptr_t)dst % elem_bytes) return ST_EALIGN;
+  if (empty) return ST_OK;
+  const Range rs{(uintptr_t)src + smin * elem_bytes, (uintptr_t)src + (smax + 1) * elem_bytes};
+  const Range rd{(uintptr_t)dst + dmin * elem_bytes, (uintptr_t)dst + (dmax + 1) * elem_bytes};
+  if (overlap(rs, rd)) return ST_EINVAL;
+  return launch_relayout(src, src_strides, dst, dst_strides, dims, ndim, elem_bytes, (hipStream_t)stream);
+}
+
+size_t st_block_sliced_workspace(int B, int T, int S, int grid_w, int C, int H, int d, int n_t, int n_s, int dtype) {
+  if (B < 1 || T < 1 || S < 1 || grid_w < 1 || C < 1 || H < 1 || d < 4 || n_t < 1 || n_s < 1 || !dtype_ok(dtype))
+    return 0;
+  if (T % n_t || S % n_s || S % grid_w) return 0;
+  return plan_block(B, T, S, grid_w, C, H, d, n_t, n_s, dtype).total;
+}
+
+st_status st_block_sliced(const void *x, int B, int T, int t_valid, int S, int grid_w, int C, int H, int d, int n_t,
+                          int n_s, const st_layer_weights *spatial, const st_layer_weights *temporal, float eps,
+                          float rope_base, int dtype, void *y, void *ws, size_t ws_bytes, void *stream) {
+  if (!dtype_ok(dtype)) return ST_EINVAL;
+  if (!x || !y || !spatial || !temporal) return ST_EINVAL;
+  for (const st_layer_weights *w : {spatial, temporal})
+    if (!w->w_qkv || !w->w_o || !w->g_q || !w->g_k) return ST_EINVAL;
+  if (B < 1 || T < 1 || S < 1 || C < 1 || H < 1 || grid_w < 1 || n_t < 1 || n_s < 1) return ST_EINVAL;
+  if (T % n_t || S % n_s || S % grid_w || t_valid < 1 || t_valid > T) return ST_EINVAL;
+  if (d < 4 || d % 4) return ST_EINVAL;
+  if (!(eps >= 0.f) || !isfinite(eps) || !(rope_base > 0.f) || !isfinite(rope_base)) return ST_EINVAL;
+  if (!head_dim_ok(d, dtype, ST_ROPE_2D)) return ST_EUNSUPPORTED;
+  if (dtype == ST_BF16 && (C % 8 || (H * d) % 8)) return ST_EUNSUPPORTED;
+  if (C % 4) return ST_EUNSUPPORTED;
+  if ((int64_t)B * T * S >= (1ll << 32) / 2) return ST_EUNSUPPORTED;
+  for (const st_layer_weights *w : {spatial, temporal})
+    for (const void *p : {w->w_qkv, w->w_o, (const void *)w->g_q, (const void *)w->g_k})
+      if (!aligned16(p)) return ST_EALIGN;
+  if (!aligned16(x) || !aligned16(y)) return ST_EALIGN;
+  const BlockPlan P = plan_block(B, T, S, grid_w, C, H, d, n_t, n_s, dtype);
+  if (!ws || ws_bytes < P.total) return ST_EWORKSPACE;
+  if (!aligned16(ws)) return ST_EALIGN;
+  const size_t e = esize(dtype);
+  const int64_t N = (int64_t)B * T * S;
+  const Range rx = rng(x, N * C * e), ry = rng(y, N * C * e), rw = rng(ws, (int64_t)P.total);
+  if (overlap(rx, ry) || overlap(ry, rw) || overlap(rx, rw)) return ST_EINVAL;
+
+  hipStream_t s = (hipStream_t)stream;
+  char *W = static_cast<char *>(ws);
+  float *rope2 = reinterpret_cast<float *>(W + P.rope2);
+  float *rope1 = reinterpret_cast<float *>(W + P.rope1);
+  void *q = W + P.q, *k = W + P.k, *v = W + P.v, *o = W + P.o;
+  st_status r = launch_rope_table(d, ST_ROPE_2D, rope_base, P.npos2, rope2, s);
+  if (r != ST_OK) return r;
+  r = launch_rope_table(d, ST_ROPE_1D, rope_base, P.npos1, rope1, s);
+  if (r != ST_OK) return r;
+  const RopeArgs r2{ST_ROPE_2D, P.npos2, rope2, S, 0, grid_w};   // rows [.., S]: h = s / W, w = s % W
+  const RopeArgs r1{ST_ROPE_1D, P.npos1, rope1, T, 0, 0};        // rows [.., T]: p = t
+  const int eb = (int)e;
+  const int64_t Cl = C;
+
+  if (n_t == 1 && n_s == 1) {
+    void *h = W + P.hb, *hs = W + P.xs;
+    r = run_layer(x, (int64_t)B * T, S, S, C, H, d, spatial, eps, r2, dtype, q, k, v, o, h, false, s);
+    if (r != ST_OK) return r;
+    {  // [B,T,S,C] -> [B,S,T,C]
+      const int64_t dims[4] = {B, T, S, C};
+      const int64_t ss[4] = {(int64_t)T * S * Cl, S * Cl, Cl, 1};
+      const int64_t ds[4] = {(int64_t)S * T * Cl, Cl, T * Cl, 1};
+      r = launch_relayout(h, ss, hs, ds, dims, 4, eb, s);
+      if (r != ST_OK) return r;
+    }
+    r = run_layer(hs, (int64_t)B * S, T, t_valid, C, H, d, temporal, eps, r1, dtype, q, k, v, o, h, true, s);
+    if (r != ST_OK) return r;
+    const int64_t dims[4] = {B, S, T, C};   // [B,S,T,C] -> [B,T,S,C]
+    const int64_t ss[4] = {(int64_t)S * T * Cl, T * Cl, Cl, 1};
+    const int64_t ds[4] = {(int64_t)T * S * Cl, Cl, S * Cl, 1};
+    return launch_relayout(h, ss, y, ds, dims, 4, eb, s);
+  }
+
+  // Sliced schedule.  Blocked layout xb[b][i][j][a][e][c] with a < T/N_T, e < S/N_S.
+  const int tt = T / n_t, ss_ = S / n_s;
+  const int64_t bstr[6] = {(int64_t)n_t * n_s * tt * ss_ * Cl, (int64_t)n_s * tt * ss_ * Cl, (int64_t)tt * ss_ * Cl,
+                           ss_ * Cl, Cl, 1};   // strides of [B, N_T, N_S, tt, ss, C]
+  void *xb = W + P.xb, *hb = W + P.hb, *xs = W + P.xs, *ys = W + P.ys;
+  {  // step 2: x [B,T,S,C] viewed as [B, N_T, tt, N_S, ss, C] -> blocked
+    const int64_t dims[6] = {B, n_t, tt, n_s, ss_, C};
+    const int64_t sx[6] = {(int64_t)T * S * Cl, (int64_t)tt * S * Cl, S * Cl, ss_ * Cl, Cl, 1};
+    const int64_t db[6] = {bstr[0], bstr[1], bstr[3], bstr[2], bstr[4], 1};
+    r = launch_relayout(x, sx, xb, db, dims, 6, eb, s);
+    if (r != ST_OK) return r;
+  }
+  // spatial layer, one time slice at a time: gather [B, tt, S, C], compute, scatter back
+  for (int i = 0; i < n_t; ++i) {
+    const int64_t dims[5] = {B, tt, n_s, ss_, C};
+    const int64_t sb[5] = {bstr[0], bstr[3], bstr[2], bstr[4], 1};
+    const int64_t sc[5] = {(int64_t)tt * S * Cl, S * Cl, ss_ * Cl, Cl, 1};
+    char *blk = static_cast<char *>(xb) + (int64_t)i * bstr[1] * eb;
+    r = launch_relayout(blk, sb, xs, sc, dims, 5, eb, s);
+    if (r != ST_OK) return r;
+    r = run_layer(xs, (int64_t)B * tt, S, S, C, H, d, spatial, eps, r2, dtype, q, k, v, o, ys, false, s);
+    if (r != ST_OK) return r;
+    char *hblk = static_cast<char *>(hb) + (int64_t)i * bstr[1] * eb;
+    r = launch_relayout(ys, sc, hblk, sb, dims, 5, eb, s);
+    if (r != ST_OK) return r;
+  }
+  // temporal layer, one space slice at a time: gather [B, ss, T, C], compute, scatter back into xb (reused as yb)
+  void *yb = xb;
+  for (int j = 0; j < n_s; ++j) {
+    const int64_t dims[5] = {B, n_t, tt, ss_, C};
+    const int64_t sb[5] = {bstr[0], bstr[1], bstr[3], bstr[4], 1};
+    const int64_t sc[5] = {(int64_t)ss_ * T * Cl, (int64_t)tt * Cl, Cl, (int64_t)T * Cl, 1};
+    const char *hblk = static_cast<const char *>(hb) + (int64_t)j * bstr[2] * eb;
+    r = launch_relayout(hblk, sb, xs, sc, dims, 5, eb, s);
+    if (r != ST_OK) return r;
+    r = run_layer(xs, (int64_t)B * ss_, T, t_valid, C, H, d, temporal, eps, r1, dtype, q, k, v, o, ys, true, s);
+    if (r != ST_OK) return r;
+    char *yblk = static_cast<char *>(yb) + (int64_t)j * bstr[2] * eb;
+    r = launch_relayout(ys, sc, yblk, sb, dims, 5, eb, s);
+    if (r != ST_OK) return r;
+  }
+  {  // step 10: blocked -> [B, T, S, C]
+    const int64_t dims[6] = {B, n_t, tt, n_s, ss_, C};
+    const int64_t sx[6] = {(int64_t)T * S * Cl, (int64_t)tt * S * Cl, S * Cl, ss_ * Cl, Cl, 1};
+    const int64_t db[6] = {bstr[0], bstr[1], bstr[3], bstr[2], bstr[4], 1};
+    return launch_relayout(yb, db, y, sx, dims, 6, eb, s);
+  }
+}
+
+}  // extern "C"

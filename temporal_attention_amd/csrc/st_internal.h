@@ -1,0 +1,84 @@
+// Internal declarations shared by the HIP sources of libst.so (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/st.h"
+
+namespace st {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint16_t u16;
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_bits_to_f32(u16 b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Two fp32 -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  f32x2 v = {a, b};
+  bf16x2 r = __builtin_convertvector(v, bf16x2);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// blockIdx.x -> logical tile id such that consecutive logical ids run on the
+// same XCD.  The dispatcher hands workgroup i to XCD i % 8; tiles that share
+// data (the N tiles of one GEMM row block, the query blocks of one attention
+// sequence) then share that XCD's L2.
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t bid, uint32_t nblocks) {
+  constexpr uint32_t kXcd = 8;
+  const uint32_t per = nblocks / kXcd;          // full round-robin rows
+  const uint32_t full = per * kXcd;
+  if (bid >= full) return bid;                  // ragged tail keeps its id
+  return (bid % kXcd) * per + bid / kXcd;
+}
+
+inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+inline st_status launch_status() {
+  return hipGetLastError() == hipSuccess ? ST_OK : ST_ELAUNCH;
+}
+
+// Launchers (each validates nothing; the C ABI layer has done it).
+st_status launch_rope_table(int d, int kind, double base, int n_pos, float *table, hipStream_t s);
+
+st_status launch_relayout(const void *src, const int64_t *src_str, void *dst, const int64_t *dst_str,
+                          const int64_t *dims, int ndim, int elem_bytes, hipStream_t s);
+
+struct RopeArgs {
+  int kind;             // st_rope_kind
+  int npos;
+  const float *table;   // [npos][pairs][2]
+  int64_t period, offset;
+  int grid_w;
+};
+
+st_status launch_qkv_bf16(const void *x, int64_t rows, int c_in, const void *w, const float *g_q,
+                          const float *g_k, float eps, const RopeArgs &rope, int H, int d, void *q,
+                          void *k, void *v, hipStream_t s);
+st_status launch_linear_bf16(const void *a, int64_t rows, int k_in, const void *w, int n_out, void *y,
+                             hipStream_t s);
+st_status launch_qkv_f32(const float *x, int64_t rows, int c_in, const float *w, const float *g_q,
+                         const float *g_k, float eps, const RopeArgs &rope, int H, int d, float *q,
+                         float *k, float *v, hipStream_t s);
+st_status launch_linear_f32(const float *a, int64_t rows, int k_in, const float *w, int n_out, float *y,
+                            hipStream_t s);
+
+// Attention over the middle axis L of [outer, L, H, d] tensors, keys j >= n_valid masked.
+st_status launch_attn_bf16(const void *q, const void *k, const void *v, int64_t outer, int L, int n_valid,
+                           int H, int d, float scale, void *out, hipStream_t s);
+st_status launch_attn_short_bf16(const void *q, const void *k, const void *v, int64_t outer, int L,
+                                 int n_valid, int H, int d, float scale, void *out, hipStream_t s);
+st_status launch_attn_f32(const float *q, const float *k, const float *v, int64_t outer, int L, int n_valid,
+                          int H, int d, float scale, float *out, hipStream_t s);
+
+bool attn_bf16_supported(int d);
+bool attn_short_supported(int L, int d);
+
+}  // namespace st

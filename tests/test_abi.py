@@ -1,0 +1,155 @@
+"""C-ABI boundary tests that need no GPU.
+
+The library must load, export every entry point include/st.h declares, and
+reject every invalid argument on the host, before any HIP call, with its
+documented status code.  Pointers here are fake aligned addresses: validation
+never dereferences them, and every case below fails validation.
+"""
+import os
+import re
+
+import pytest
+
+import temporal_attention_amd as st
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+P = 0x10000          # fake 16-byte-aligned device addresses, far apart
+P2, P3, P4, P5, P6, P7 = (P * k for k in range(2, 8))
+BIG = 1 << 40        # far-apart region for outputs
+
+
+def declared_functions():
+    with open(os.path.join(ROOT, "include", "st.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(st_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(st.lib, n), n
+    assert sorted(st.EXPORTS) == names
+
+
+def test_status_strings():
+    assert st.st_status_str(0) == "ok"
+    assert "invalid" in st.st_status_str(1)
+    assert st.st_status_str(99) == "unknown status"
+
+
+def code(fn, *args):
+    with pytest.raises(st.STError) as e:
+        fn(*args, stream=0)
+    return e.value.code
+
+
+def test_rope_table_validation():
+    assert st.st_rope_table_floats(72, st.ST_ROPE_2D, 120) == 120 * 18 * 2
+    assert st.st_rope_table_floats(72, st.ST_ROPE_1D, 52) == 52 * 36 * 2
+    assert code(st.st_rope_table, 72, 0, 10000.0, 10, P) == st.ST_EINVAL            # kind none
+    assert code(st.st_rope_table, 70, st.ST_ROPE_2D, 10000.0, 10, P) == st.ST_EINVAL  # d % 4
+    assert code(st.st_rope_table, 72, st.ST_ROPE_1D, -1.0, 10, P) == st.ST_EINVAL
+    assert code(st.st_rope_table, 72, st.ST_ROPE_1D, 10000.0, 0, P) == st.ST_EINVAL
+    assert code(st.st_rope_table, 72, st.ST_ROPE_1D, 10000.0, 10, None) == st.ST_EINVAL
+    assert code(st.st_rope_table, 72, st.ST_ROPE_1D, 10000.0, 10, P + 4) == st.ST_EALIGN
+
+
+def qkv_args(**kw):
+    a = dict(x=P, rows=100, c_in=1152, w_qkv=P2, g_q=P3, g_k=P4, eps=1e-6, rope_kind=st.ST_ROPE_2D, rope_table=P5,
+             rope_npos=120, pos_period=8160, pos_offset=0, grid_w=120, H=16, d=72, dtype=st.ST_BF16, q=BIG,
+             k=2 * BIG, v=3 * BIG)
+    a.update(kw)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(x=None), st.ST_EINVAL),
+    (dict(g_q=None), st.ST_EINVAL),
+    (dict(dtype=7), st.ST_EINVAL),
+    (dict(rows=-1), st.ST_EINVAL),
+    (dict(eps=-1.0), st.ST_EINVAL),
+    (dict(d=70), st.ST_EINVAL),                       # 2D RoPE needs d % 4 == 0
+    (dict(d=96), st.ST_EUNSUPPORTED),                 # no bf16 kernel for d = 96
+    (dict(d=256, dtype=st.ST_F32), st.ST_EUNSUPPORTED),
+    (dict(c_in=1150), st.ST_EUNSUPPORTED),            # bf16 needs c_in % 8 == 0
+    (dict(rope_kind=5), st.ST_EINVAL),
+    (dict(rope_table=None), st.ST_EINVAL),
+    (dict(rope_npos=60, rows=8160), st.ST_EINVAL),   # h up to 67 not in table
+    (dict(rope_kind=st.ST_ROPE_1D, rope_npos=51, pos_period=52), st.ST_EINVAL),
+    (dict(pos_period=0), st.ST_EINVAL),
+    (dict(rope_table=P5 + 8), st.ST_EALIGN),
+    (dict(x=P + 2), st.ST_EALIGN),
+    (dict(q=P), st.ST_EINVAL),                        # q aliases x
+    (dict(k=BIG + 64), st.ST_EINVAL),                 # k overlaps q
+])
+def test_qkv_validation(kw, want):
+    assert code(st.st_qkv_norm_rope, *qkv_args(**kw)) == want
+
+
+@pytest.mark.parametrize("args,want", [
+    ((None, 10, 1152, P2, 1152, st.ST_BF16, BIG), st.ST_EINVAL),
+    ((P, 10, 1152, P2, 1150, st.ST_BF16, BIG), st.ST_EUNSUPPORTED),
+    ((P, 10, 1151, P2, 1152, st.ST_BF16, BIG), st.ST_EUNSUPPORTED),
+    ((P, 10, 1152, P2, 1152, 3, BIG), st.ST_EINVAL),
+    ((P, 10, 1152, P2, 1152, st.ST_BF16, P + 16), st.ST_EINVAL),    # y overlaps a
+    ((P, 10, 1152, P2, 1152, st.ST_BF16, BIG + 2), st.ST_EALIGN),
+])
+def test_out_proj_validation(args, want):
+    assert code(st.st_out_proj, *args) == want
+
+
+@pytest.mark.parametrize("args,want", [
+    ((None, P2, P3, 1, 51, 8160, 16, 72, 0.1, st.ST_BF16, BIG), st.ST_EINVAL),
+    ((P, P2, P3, 1, 51, 8160, 16, 72, 0.0, st.ST_BF16, BIG), st.ST_EINVAL),       # scale must be > 0
+    ((P, P2, P3, 1, 51, 8160, 16, 72, float("nan"), st.ST_BF16, BIG), st.ST_EINVAL),
+    ((P, P2, P3, -1, 51, 8160, 16, 72, 0.1, st.ST_BF16, BIG), st.ST_EINVAL),
+    ((P, P2, P3, 1, 51, 8160, 16, 80, 0.1, st.ST_BF16, BIG), st.ST_EUNSUPPORTED),
+    ((P, P2, P3, 1, 51, 8160, 16, 72, 0.1, st.ST_BF16, P), st.ST_EINVAL),         # out aliases q
+    ((P, P2, P3, 1, 51, 8160, 16, 72, 0.1, st.ST_BF16, BIG + 8), st.ST_EALIGN),
+])
+def test_attn_spatial_validation(args, want):
+    assert code(st.st_attn_spatial, *args) == want
+
+
+@pytest.mark.parametrize("t_valid,want", [(0, st.ST_EINVAL), (53, st.ST_EINVAL)])
+def test_attn_temporal_validation(t_valid, want):
+    assert code(st.st_attn_temporal, P, P2, P3, 1, 8160, 52, t_valid, 16, 72, 0.1, st.ST_BF16, BIG) == want
+
+
+def test_relayout_validation():
+    dims, s1, s2 = [2, 3, 4], [12, 4, 1], [12, 1, 3]
+    assert code(st.st_relayout, None, s1, BIG, s2, dims, 3, 2) == st.ST_EINVAL
+    assert code(st.st_relayout, P, s1, BIG, s2, dims, 0, 2) == st.ST_EINVAL           # ndim
+    assert code(st.st_relayout, P, s1 * 3, BIG, s2 * 3, dims * 3, 7, 2) == st.ST_EINVAL
+    assert code(st.st_relayout, P, s1, BIG, s2, dims, 3, 3) == st.ST_EINVAL           # elem_bytes
+    assert code(st.st_relayout, P, s1, P, s2, dims, 3, 2) == st.ST_EINVAL             # src == dst
+    assert code(st.st_relayout, P, s1, P + 8, s2, dims, 3, 2) == st.ST_EINVAL         # overlap
+    assert code(st.st_relayout, P, s1, BIG, s2, [2, -3, 4], 3, 2) == st.ST_EINVAL
+    assert code(st.st_relayout, P + 1, s1, BIG, s2, dims, 3, 2) == st.ST_EALIGN
+
+
+def test_block_workspace_and_validation():
+    ws = st.st_block_sliced_workspace(1, 52, 8160, 120, 1152, 16, 72, 4, 4, st.ST_BF16)
+    assert ws > 2 * 52 * 8160 * 1152 * 2
+    assert st.st_block_sliced_workspace(1, 51, 8160, 120, 1152, 16, 72, 4, 4, st.ST_BF16) == 0   # T % n_t
+    w = st.layer_weights(P, P2, P3, P4)
+    bad_w = st.layer_weights(P, None, P3, P4)
+    base = dict(x=P5, B=1, T=52, t_valid=51, S=8160, grid_w=120, C_=1152, H=16, d=72, n_t=4, n_s=4, spatial=w,
+                temporal=w, eps=1e-6, rope_base=10000.0, dtype=st.ST_BF16, y=BIG, ws=2 * BIG, ws_bytes=ws)
+
+    def c(**kw):
+        a = dict(base)
+        a.update(kw)
+        return code(st.st_block_sliced, *a.values())
+    assert c(T=51) == st.ST_EINVAL                 # T % n_t
+    assert c(t_valid=0) == st.ST_EINVAL
+    assert c(grid_w=121) == st.ST_EINVAL           # S % grid_w
+    assert c(spatial=None) == st.ST_EINVAL
+    assert c(temporal=bad_w) == st.ST_EINVAL
+    assert c(ws_bytes=ws - 1) == st.ST_EWORKSPACE
+    assert c(ws=None) == st.ST_EWORKSPACE
+    assert c(d=80) == st.ST_EUNSUPPORTED
+    assert c(y=P5) == st.ST_EINVAL                 # y aliases x
+    assert c(x=P5 + 2) == st.ST_EALIGN

@@ -1,0 +1,245 @@
+"""Block-level parity on the GPU: the layer pair against the fp64 oracle, the
+slicing schedule against the unsliced run, and sampled parity at the full
+720p / 1080p / 4096px workload sizes in the launch configuration the
+benchmark times.
+
+Per-layer checks feed the oracle the same bf16 tensors the GPU layer saw, so
+errors do not compound; the end-to-end comparison is checked too.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import st_synth
+from helpers import assert_close, empty, errors, f64, to_dev, to_host, torch
+
+pytestmark = pytest.mark.gpu
+
+t_ = torch()
+if not t_.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import temporal_attention_amd as st  # noqa: E402
+from temporal_attention_amd.pipeline import LayerPair  # noqa: E402
+
+EPS, BASE = st_synth.EPS, st_synth.ROPE_BASE
+
+
+def small_inputs(seed, T, S, C, H, d, dtype="bf16"):
+    x = st_synth.randn((1, T, S, C), seed, dtype=dtype)
+    w = {}
+    for i, tag in enumerate(("s", "t")):
+        w[tag] = dict(w_qkv=st_synth.randn((3 * H * d, C), seed + 10 + i, std=0.02, dtype=dtype),
+                      w_o=st_synth.randn((C, H * d), seed + 20 + i, std=0.02, dtype=dtype),
+                      g_q=np.ones(d, np.float32), g_k=np.ones(d, np.float32))
+    return x, w
+
+
+def dev_weights(w):
+    return {k: to_dev(v) for k, v in w.items()}
+
+
+def host_weights(w):
+    return dict(w_qkv=f64(w["w_qkv"]), w_o=f64(w["w_o"]), g_q=w["g_q"].astype(np.float64),
+                g_k=w["g_k"].astype(np.float64))
+
+
+def run_block(xd, wd, T, t_valid, S, grid_w, C, H, d, n_t, n_s, dt):
+    sp = st.layer_weights(wd["s"]["w_qkv"], wd["s"]["w_o"], wd["s"]["g_q"], wd["s"]["g_k"])
+    tp = st.layer_weights(wd["t"]["w_qkv"], wd["t"]["w_o"], wd["t"]["g_q"], wd["t"]["g_k"])
+    nbytes = st.st_block_sliced_workspace(1, T, S, grid_w, C, H, d, n_t, n_s, dt)
+    ws = t_.empty(nbytes, dtype=t_.uint8, device="cuda")
+    y = empty((1, T, S, C), dt == st.ST_BF16)
+    st.st_block_sliced(xd, 1, T, t_valid, S, grid_w, C, H, d, n_t, n_s, sp, tp, EPS, BASE, dt, y, ws, nbytes)
+    t_.cuda.synchronize()
+    return y
+
+
+def check_layer_pair_stepwise(lp, x_dev, wh, grid_w, sample_rows=None, attn_check=None, temporal_check=None):
+    """Run lp's steps one at a time; check each against the oracle on the GPU's own inputs."""
+    B, T, S, C, H, d = lp.B, lp.T, lp.S, lp.C, lp.H, lp.d
+    bf = lp.dtype == st.ST_BF16
+    steps = dict(lp.steps(x_dev))
+    rows = np.arange(lp.N) if sample_rows is None else sample_rows
+    rows_d = t_.as_tensor(rows, device="cuda")
+    sel = lambda t: f64(t.reshape(lp.N, -1).index_select(0, rows_d))   # noqa: E731  gather on the device first
+    res = {}
+
+    def qkv_check(src_dev, w, kind, pos_of_rows, tag):
+        qg, kg, vg = (sel(t).reshape(-1, H, d) for t in (lp.q, lp.k, lp.v))
+        xs = sel(src_dev)
+        oq, ok, ov = oracle.qkv_norm_rope(xs, w["w_qkv"], w["g_q"], w["g_k"], EPS, H, d, kind, pos_of_rows, BASE)
+        for name, g, r in (("q", qg, oq), ("k", kg, ok), ("v", vg, ov)):
+            res[f"{tag}_{name}"] = assert_close(g, r, bf, f"{tag} {name}")
+
+    # spatial layer
+    steps["qkv_spatial"]()
+    t_.cuda.synchronize()
+    s_idx = rows % S
+    qkv_check(x_dev, wh["s"], "2d", np.stack([s_idx // grid_w, s_idx % grid_w], 1), "spatial")
+    steps["attn_spatial"]()
+    t_.cuda.synchronize()
+    q5, k5, v5, o5 = (t.view(B, T, S, H, d) for t in (lp.q, lp.k, lp.v, lp.o))
+    pairs = attn_check if attn_check is not None else [(t, h) for t in range(T) for h in range(H)]
+    for (tt, hh) in pairs:
+        ref = oracle.attention(f64(q5[0, tt, :, hh]), f64(k5[0, tt, :, hh]), f64(v5[0, tt, :, hh]), lp.scale)
+        res[f"attn_s_{tt}_{hh}"] = assert_close(f64(o5[0, tt, :, hh]), ref, bf, f"spatial attn t={tt} h={hh}")
+    steps["proj_spatial"]()
+    t_.cuda.synchronize()
+    res["proj_s"] = assert_close(sel(lp.h), oracle.linear(sel(lp.o), wh["s"]["w_o"]), bf, "spatial proj")
+    steps["relayout_fwd"]()
+    t_.cuda.synchronize()
+    h_host = to_host(lp.h).reshape(B, T, S, C)
+    assert np.array_equal(to_host(lp.hs).reshape(B, S, T, C), oracle.bt_to_bs(h_host)), "relayout fwd"
+    del h_host
+    # temporal layer (rows are [B, S, T])
+    steps["qkv_temporal"]()
+    t_.cuda.synchronize()
+    qkv_check(lp.hs, wh["t"], "1d", rows % T, "temporal")
+    steps["attn_temporal"]()
+    t_.cuda.synchronize()
+    q5, k5, v5, o5 = (t.view(B, S, T, H, d) for t in (lp.q, lp.k, lp.v, lp.o))
+    patches = t_.as_tensor(temporal_check if temporal_check is not None else np.arange(S), device="cuda")
+    qs, ks, vs, os_ = (f64(t.index_select(1, patches)) for t in (q5, k5, v5, o5))
+    ref = oracle.attn_temporal(qs, ks, vs, lp.scale, lp.t_valid)
+    res["attn_t"] = assert_close(os_, ref, bf, "temporal attn")
+    steps["proj_temporal"]()
+    t_.cuda.synchronize()
+    res["proj_t"] = assert_close(sel(lp.h), oracle.linear(sel(lp.o), wh["t"]["w_o"]), bf, "temporal proj")
+    steps["relayout_bwd"]()
+    t_.cuda.synchronize()
+    assert np.array_equal(to_host(lp.y).reshape(B, T, S, C), oracle.bs_to_bt(to_host(lp.h).reshape(B, S, T, C))), \
+        "relayout bwd"
+    return res
+
+
+@pytest.mark.parametrize("T,S,grid_w,C,H,d", [(6, 48, 8, 1152, 16, 72), (3, 100, 10, 384, 3, 128), (4, 36, 6, 128, 2, 64)])
+def test_layer_pair_bf16_stepwise_and_end_to_end(T, S, grid_w, C, H, d):
+    x, w = small_inputs(100 + T + S, T, S, C, H, d)
+    xd = to_dev(x)
+    wd = {k: dev_weights(v) for k, v in w.items()}
+    wh = {k: host_weights(v) for k, v in w.items()}
+    lp = LayerPair(1, T, S, grid_w, C, H, d)
+    lp.set_weights(wd["s"], wd["t"])
+    check_layer_pair_stepwise(lp, xd, wh, grid_w)
+    y_ref = oracle.block(f64(x), wh["s"], wh["t"], H, d, grid_w, EPS, BASE)
+    assert_close(f64(lp.y).reshape(y_ref.shape), y_ref, True, "block end to end")
+    # the native orchestration runs the same launches: bit-identical
+    yb = run_block(xd, wd, T, T, S, grid_w, C, H, d, 1, 1, st.ST_BF16)
+    assert t_.equal(yb.view(-1), lp.y.view(-1))
+
+
+@pytest.mark.parametrize("n_t,n_s", [(2, 2), (3, 4), (6, 1), (1, 8), (2, 24)])
+def test_sliced_equals_unsliced_bf16(n_t, n_s):
+    T, S, grid_w, C, H, d = 6, 48, 8, 1152, 16, 72
+    x, w = small_inputs(7, T, S, C, H, d)
+    xd = to_dev(x)
+    wd = {k: dev_weights(v) for k, v in w.items()}
+    y1 = run_block(xd, wd, T, T, S, grid_w, C, H, d, 1, 1, st.ST_BF16)
+    ys = run_block(xd, wd, T, T, S, grid_w, C, H, d, n_t, n_s, st.ST_BF16)
+    assert t_.equal(y1, ys)
+
+
+def test_padded_masked_schedule_equals_unpadded():
+    T, S, grid_w, C, H, d = 5, 48, 8, 1152, 16, 72
+    x, w = small_inputs(8, T, S, C, H, d)
+    xp = np.concatenate([x, np.zeros_like(x[:, :1])], axis=1)
+    wd = {k: dev_weights(v) for k, v in w.items()}
+    y1 = run_block(to_dev(x), wd, T, T, S, grid_w, C, H, d, 1, 1, st.ST_BF16)
+    yp = run_block(to_dev(xp), wd, T + 1, T, S, grid_w, C, H, d, 2, 4, st.ST_BF16)
+    assert t_.equal(yp[:, :T], y1)
+    wh = {k: host_weights(v) for k, v in w.items()}
+    y_ref = oracle.block_sliced(f64(xp), wh["s"], wh["t"], H, d, grid_w, EPS, BASE, 2, 4, t_valid=T)
+    assert_close(f64(yp)[:, :T], y_ref[:, :T], True, "padded block")
+
+
+def test_tiny_fp32_workload_block():
+    inp = st_synth.make_inputs(1)
+    c = inp["cfg"]
+    T, S, grid_w, C, H, d = c["T"], c["S"], c["grid_w"], c["C"], c["H"], c["d"]
+    w = {"s": dict(w_qkv=inp["w_qkv_s"], w_o=inp["w_o_s"], g_q=inp["g_q"], g_k=inp["g_k"]),
+         "t": dict(w_qkv=inp["w_qkv_t"], w_o=inp["w_o_t"], g_q=inp["g_q"], g_k=inp["g_k"])}
+    wd = {k: dev_weights(v) for k, v in w.items()}
+    wh = {k: host_weights(v) for k, v in w.items()}
+    xd = to_dev(inp["x"])
+    lp = LayerPair(1, T, S, grid_w, C, H, d, dtype=st.ST_F32)
+    lp.set_weights(wd["s"], wd["t"])
+    check_layer_pair_stepwise(lp, xd, wh, grid_w)
+    y_ref = oracle.block(f64(inp["x"]), wh["s"], wh["t"], H, d, grid_w, EPS, BASE)
+    assert_close(f64(lp.y).reshape(y_ref.shape), y_ref, False, "fp32 block")
+    y1 = run_block(xd, wd, T, T, S, grid_w, C, H, d, 1, 1, st.ST_F32)
+    y2 = run_block(xd, wd, T, T, S, grid_w, C, H, d, 2, 2, st.ST_F32)
+    assert t_.equal(y1.view(-1), lp.y.view(-1))
+    assert t_.equal(y1, y2)
+
+
+def full_size(cfg_id, attn_pairs, n_rows=96, n_patches=48):
+    inp = st_synth.make_inputs(cfg_id)
+    c = inp["cfg"]
+    B, T, S, grid_w, C, H, d = c["B"], c["T"], c["S"], c["grid_w"], c["C"], c["H"], c["d"]
+    w = {"s": dict(w_qkv=inp["w_qkv_s"], w_o=inp["w_o_s"], g_q=inp["g_q"], g_k=inp["g_k"]),
+         "t": dict(w_qkv=inp["w_qkv_t"], w_o=inp["w_o_t"], g_q=inp["g_q"], g_k=inp["g_k"])}
+    wd = {k: dev_weights(v) for k, v in w.items()}
+    wh = {k: host_weights(v) for k, v in w.items()}
+    xd = to_dev(inp["x"])
+    del inp
+    lp = LayerPair(B, T, S, grid_w, C, H, d)
+    lp.set_weights(wd["s"], wd["t"])
+    rng = np.random.default_rng(cfg_id)
+    rows = np.sort(rng.choice(lp.N, n_rows, replace=False))
+    patches = np.sort(rng.choice(S, min(n_patches, S), replace=False))
+    res = check_layer_pair_stepwise(lp, xd, wh, grid_w, sample_rows=rows, attn_check=attn_pairs,
+                                    temporal_check=patches)
+    return lp, xd, wd, res, (T, S, grid_w, C, H, d)
+
+
+def test_720p_full_size_sampled():
+    full_size(2, attn_pairs=[(0, 0), (23, 15)])
+
+
+def test_1080p_full_size_sampled_and_sliced_schedule():
+    lp, xd, wd, res, (T, S, grid_w, C, H, d) = full_size(3, attn_pairs=[(0, 0), (50, 15)])
+    print({k: (round(a, 5), round(r, 5)) for k, (a, r) in res.items()})
+    y3 = lp.y.view(1, T, S, C)
+    yb = run_block(xd, wd, T, T, S, grid_w, C, H, d, 1, 1, st.ST_BF16)
+    assert t_.equal(yb, y3)
+    del lp, yb
+    t_.cuda.empty_cache()
+    # the pages' schedule: T padded to 52 with a zero frame, N_T = N_S = 4
+    x4 = t_.cat([xd, t_.zeros_like(xd[:, :1])], dim=1)
+    y4 = run_block(x4, wd, T + 1, T, S, grid_w, C, H, d, 4, 4, st.ST_BF16)
+    assert t_.equal(y4[:, :T], y3)
+
+
+def test_4096px_image_attention_sampled():
+    """Image-DiT full self-attention at 65,536 tokens, 3 heads x 128 (spatial layer with T = 1)."""
+    inp = st_synth.make_inputs(5)
+    c = inp["cfg"]
+    S, grid_w, C, H, d = c["S"], c["grid_w"], c["C"], c["H"], c["d"]
+    xd = to_dev(inp["x"])
+    wq, wo = to_dev(inp["w_qkv_s"]), to_dev(inp["w_o_s"])
+    g = to_dev(inp["g_q"])
+    npos = max(S // grid_w, grid_w)
+    tab = t_.empty(st.st_rope_table_floats(d, st.ST_ROPE_2D, npos), dtype=t_.float32, device="cuda")
+    st.st_rope_table(d, st.ST_ROPE_2D, BASE, npos, tab)
+    q, k, v, o = (empty((S, H, d)) for _ in range(4))
+    st.st_qkv_norm_rope(xd, S, C, wq, g, g, EPS, st.ST_ROPE_2D, tab, npos, S, 0, grid_w, H, d, st.ST_BF16, q, k, v)
+    st.st_attn_spatial(q, k, v, 1, 1, S, H, d, 1 / math.sqrt(d), st.ST_BF16, o)
+    y = empty((S, C))
+    st.st_out_proj(o, S, H * d, wo, C, st.ST_BF16, y)
+    t_.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    rows = np.sort(rng.choice(S, 128, replace=False))
+    pos = np.stack([rows // grid_w, rows % grid_w], 1)
+    oq, ok, ov = oracle.qkv_norm_rope(f64(inp["x"]).reshape(S, C)[rows], f64(inp["w_qkv_s"]), np.ones(d), np.ones(d),
+                                      EPS, H, d, "2d", pos, BASE)
+    for name, gt, r in (("q", q, oq), ("k", k, ok), ("v", v, ov)):
+        assert_close(f64(gt)[rows], r, True, name)
+    kk, vv = f64(k), f64(v)
+    for h in range(H):   # sampled queries against all 65,536 keys
+        ref = oracle.attention(f64(q)[rows, h], kk[:, h], vv[:, h], 1 / math.sqrt(d))
+        assert_close(f64(o)[rows, h], ref, True, f"attn h={h}")
+    assert_close(f64(y)[rows], oracle.linear(f64(o)[rows].reshape(len(rows), -1), f64(inp["w_o_s"])), True, "proj")
+    print("errors", errors(f64(o)[rows, 0], oracle.attention(f64(q)[rows, 0], kk[:, 0], vv[:, 0], 1 / math.sqrt(d))))

@@ -1,0 +1,272 @@
+"""Kernel-level parity: each C-ABI entry point on the GPU against the fp64 oracle.
+
+Inputs are seeded (st_synth), identical bytes on both sides.  Shapes span
+several tiles with ragged tails (L not a multiple of 64 or 256, T = 51/52,
+rows not a multiple of 128) plus the degenerate cases (L = 1, T = 1).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import st_synth
+from helpers import assert_close, empty, f64, to_dev, to_host, torch
+
+pytestmark = pytest.mark.gpu
+
+t_ = torch()
+if not t_.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import temporal_attention_amd as st  # noqa: E402
+
+BF, F32 = st.ST_BF16, st.ST_F32
+
+
+def sync():
+    t_.cuda.synchronize()
+
+
+# --------------------------------------------------------------------------- #
+# Relayout: bit-exact                                                          #
+# --------------------------------------------------------------------------- #
+NP_T = {1: np.uint8, 2: np.uint16, 4: np.uint32, 8: np.uint64, 16: np.dtype((np.void, 16))}
+
+
+def run_relayout(src_np, dims, sstr, dstr, dst_elems, eb):
+    """Upload src (flat array of element type), run st_relayout, return dst and expected."""
+    src = t_.from_numpy(np.frombuffer(src_np.tobytes(), dtype=np.uint8).copy()).cuda()
+    dst = t_.full((dst_elems * eb,), 0xA5, dtype=t_.uint8, device="cuda")
+    st.st_relayout(src, sstr, dst, dstr, dims, len(dims), eb)
+    sync()
+    got = np.frombuffer(dst.cpu().numpy().tobytes(), dtype=NP_T[eb])
+    exp = np.frombuffer(np.full(dst_elems * eb, 0xA5, np.uint8).tobytes(), dtype=NP_T[eb]).copy()
+    idx = np.indices(dims).reshape(len(dims), -1)
+    so = (np.asarray(sstr)[:, None] * idx).sum(0)
+    do = (np.asarray(dstr)[:, None] * idx).sum(0)
+    exp[do] = src_np[so]
+    return got, exp
+
+
+def contiguous_strides(shape):
+    s = [1] * len(shape)
+    for i in range(len(shape) - 2, -1, -1):
+        s[i] = s[i + 1] * shape[i + 1]
+    return s
+
+
+@pytest.mark.parametrize("B,T,S,C,eb", [(1, 5, 37, 1152, 2), (2, 4, 6, 24, 4), (1, 51, 13, 72, 2), (1, 3, 7, 5, 2),
+                                        (1, 2, 3, 8, 1), (1, 3, 4, 6, 8), (1, 2, 5, 3, 16)])
+def test_relayout_bt_to_bs(B, T, S, C, eb):
+    rng = np.random.default_rng(B * 1000 + T * 100 + S + C)
+    n = B * T * S * C
+    src = np.frombuffer(rng.integers(0, 256, n * eb, dtype=np.uint8).tobytes(), dtype=NP_T[eb])
+    sstr = contiguous_strides([B, T, S, C])
+    dstr = [S * T * C, C, T * C, 1]
+    got, exp = run_relayout(src, [B, T, S, C], sstr, dstr, n, eb)
+    assert got.tobytes() == exp.tobytes()
+    if eb == 2:   # and it is exactly the oracle's index map
+        want = oracle.bt_to_bs(src.reshape(B, T, S, C)).reshape(-1)
+        assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("T,S,C,nt,ns", [(8, 12, 16, 2, 3), (52, 40, 72, 4, 4), (4, 6, 1152, 4, 2)])
+def test_relayout_blocked_matches_oracle(T, S, C, nt, ns):
+    rng = np.random.default_rng(T + S + C)
+    x = rng.integers(0, 65536, (1, T, S, C), dtype=np.uint16)
+    tt, ss = T // nt, S // ns
+    dims = [1, nt, tt, ns, ss, C]
+    sx = [T * S * C, tt * S * C, S * C, ss * C, C, 1]
+    bstr = contiguous_strides([1, nt, ns, tt, ss, C])
+    db = [bstr[0], bstr[1], bstr[3], bstr[2], bstr[4], 1]
+    got, _ = run_relayout(x.reshape(-1), dims, sx, db, x.size, 2)
+    assert np.array_equal(got, oracle.to_blocked(x, nt, ns).reshape(-1))
+    # and back
+    back, _ = run_relayout(got, dims, db, sx, x.size, 2)
+    assert np.array_equal(back, x.reshape(-1))
+
+
+@pytest.mark.parametrize("shape,perm,eb", [((5, 7, 3), (2, 1, 0), 2), ((4, 9), (1, 0), 4), ((3, 4, 5, 6), (3, 0, 2, 1), 1),
+                                           ((1 << 20,), (0,), 2), ((2, 1, 3), (1, 2, 0), 2)])
+def test_relayout_general_permutations(shape, perm, eb):
+    rng = np.random.default_rng(len(shape) * 7 + eb)
+    n = int(np.prod(shape))
+    src = np.frombuffer(rng.integers(0, 256, n * eb, dtype=np.uint8).tobytes(), dtype=NP_T[eb])
+    out_shape = [shape[p] for p in perm]
+    ostr = contiguous_strides(out_shape)
+    dstr = [0] * len(shape)
+    for j, p in enumerate(perm):
+        dstr[p] = ostr[j]
+    got, exp = run_relayout(src, list(shape), contiguous_strides(list(shape)), dstr, n, eb)
+    assert got.tobytes() == exp.tobytes()
+    assert np.array_equal(got.reshape(out_shape), np.transpose(src.reshape(shape), perm))
+
+
+def test_relayout_empty_is_noop():
+    src = t_.zeros(16, dtype=t_.uint8, device="cuda")
+    dst = t_.full((16,), 7, dtype=t_.uint8, device="cuda")
+    st.st_relayout(src, [4, 1], dst, [1, 4], [0, 4], 2, 1)
+    sync()
+    assert bool((dst == 7).all())
+
+
+# --------------------------------------------------------------------------- #
+# RoPE table                                                                   #
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("d,kind,npos", [(72, st.ST_ROPE_2D, 120), (72, st.ST_ROPE_1D, 52), (128, st.ST_ROPE_2D, 256),
+                                         (64, st.ST_ROPE_1D, 5)])
+def test_rope_table(d, kind, npos):
+    n = st.st_rope_table_floats(d, kind, npos)
+    tab = t_.empty(n, dtype=t_.float32, device="cuda")
+    st.st_rope_table(d, kind, 10000.0, npos, tab)
+    sync()
+    m = d // 2 if kind == st.ST_ROPE_2D else d
+    i = np.arange(m // 2)
+    theta = np.arange(npos)[:, None] * 10000.0 ** (-2.0 * i / m)
+    want = np.stack([np.cos(theta), np.sin(theta)], -1).astype(np.float32).reshape(-1)
+    got = tab.cpu().numpy()
+    assert np.max(np.abs(got.astype(np.float64) - want)) <= 1.2e-7
+
+
+# --------------------------------------------------------------------------- #
+# QKV projection + RMSNorm + RoPE                                              #
+# --------------------------------------------------------------------------- #
+def rope_positions(rows, kind, period, offset, grid_w):
+    i = np.arange(rows) % period + offset
+    if kind == st.ST_ROPE_2D:
+        return np.stack([i // grid_w, i % grid_w], 1)
+    return i
+
+
+QKV_CASES = [
+    # rows, C, H, d, kind, period, offset, grid_w, dtype
+    (300, 1152, 16, 72, st.ST_ROPE_2D, 100, 0, 10, BF),
+    (130, 1152, 16, 72, st.ST_ROPE_1D, 51, 0, 0, BF),
+    (257, 1152, 16, 72, st.ST_ROPE_NONE, 1, 0, 0, BF),
+    (200, 384, 3, 128, st.ST_ROPE_2D, 65536, 40000, 256, BF),
+    (150, 128, 2, 64, st.ST_ROPE_2D, 64, 0, 8, BF),
+    (64, 128, 2, 64, st.ST_ROPE_2D, 64, 0, 8, F32),
+    (77, 96, 3, 36, st.ST_ROPE_1D, 10, 3, 0, F32),
+]
+
+
+@pytest.mark.parametrize("rows,C,H,d,kind,period,offset,grid_w,dt", QKV_CASES)
+def test_qkv_norm_rope(rows, C, H, d, kind, period, offset, grid_w, dt):
+    sd = "bf16" if dt == BF else "f32"
+    x = st_synth.randn((rows, C), 11 + rows, dtype=sd)
+    w = st_synth.randn((3 * H * d, C), 12 + rows, std=0.02, dtype=sd)
+    rng = np.random.default_rng(rows)
+    g_q = (1.0 + 0.2 * rng.standard_normal(d)).astype(np.float32)
+    g_k = (1.0 + 0.2 * rng.standard_normal(d)).astype(np.float32)
+    pos = rope_positions(rows, kind, period, offset, grid_w)
+    npos = int(pos.max()) + 1 if kind != st.ST_ROPE_NONE else 1
+    tab = None
+    if kind != st.ST_ROPE_NONE:
+        tab = t_.empty(st.st_rope_table_floats(d, kind, npos), dtype=t_.float32, device="cuda")
+        st.st_rope_table(d, kind, 10000.0, npos, tab)
+    q, k, v = (empty((rows, H, d), dt == BF) for _ in range(3))
+    st.st_qkv_norm_rope(to_dev(x), rows, C, to_dev(w), to_dev(g_q), to_dev(g_k), 1e-6, kind, tab, npos, period, offset,
+                        grid_w, H, d, dt, q, k, v)
+    sync()
+    rk = {st.ST_ROPE_NONE: "none", st.ST_ROPE_1D: "1d", st.ST_ROPE_2D: "2d"}[kind]
+    oq, ok, ov = oracle.qkv_norm_rope(f64(x), f64(w), g_q, g_k, 1e-6, H, d, rk, pos, 10000.0)
+    for name, got, ref in (("q", q, oq), ("k", k, ok), ("v", v, ov)):
+        assert_close(f64(got), ref, bf16=dt == BF, what=name)
+
+
+def test_qkv_zero_rows_is_noop():
+    q = empty((1, 16, 72))
+    q.fill_(3.0)
+    dummy = empty((8, 1152))
+    w = empty((3 * 16 * 72, 1152))
+    g = t_.ones(72, device="cuda")
+    st.st_qkv_norm_rope(dummy, 0, 1152, w, g, g, 1e-6, st.ST_ROPE_NONE, None, 0, 1, 0, 0, 16, 72, BF, q, empty((1, 16, 72)),
+                        empty((1, 16, 72)))
+    sync()
+    assert bool((q.float() == 3.0).all())
+
+
+# --------------------------------------------------------------------------- #
+# Output projection                                                            #
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("rows,K,N,dt", [(300, 1152, 1152, BF), (129, 384, 384, BF), (50, 1152, 100, BF),
+                                         (64, 128, 128, F32)])
+def test_out_proj(rows, K, N, dt):
+    sd = "bf16" if dt == BF else "f32"
+    a = st_synth.randn((rows, K), 21 + rows, dtype=sd)
+    w = st_synth.randn((N, K), 22 + rows, std=0.02, dtype=sd)
+    y = empty((rows, N), dt == BF)
+    st.st_out_proj(to_dev(a), rows, K, to_dev(w), N, dt, y)
+    sync()
+    assert_close(f64(y), oracle.linear(f64(a), f64(w)), bf16=dt == BF, what="y")
+
+
+# --------------------------------------------------------------------------- #
+# Attention                                                                    #
+# --------------------------------------------------------------------------- #
+def qkv_tensors(shape, seed, dt, q_std=1.0):
+    sd = "bf16" if dt == BF else "f32"
+    return (st_synth.randn(shape, seed, std=q_std, dtype=sd), st_synth.randn(shape, seed + 1, dtype=sd),
+            st_synth.randn(shape, seed + 2, dtype=sd))
+
+
+SPATIAL_CASES = [
+    # B, T, S, H, d, q_std, dtype
+    (1, 2, 300, 2, 72, 1.0, BF),
+    (2, 1, 1000, 1, 72, 3.0, BF),      # peaked softmax
+    (1, 1, 1, 3, 72, 1.0, BF),         # L = 1
+    (1, 3, 64, 2, 72, 1.0, BF),
+    (1, 1, 700, 3, 128, 1.0, BF),
+    (1, 2, 257, 2, 64, 2.0, BF),
+    (1, 2, 64, 2, 64, 1.0, F32),
+]
+
+
+@pytest.mark.parametrize("B,T,S,H,d,q_std,dt", SPATIAL_CASES)
+def test_attn_spatial(B, T, S, H, d, q_std, dt):
+    q, k, v = qkv_tensors((B, T, S, H, d), 31 + S + d, dt, q_std)
+    out = empty((B, T, S, H, d), dt == BF)
+    scale = 1.0 / math.sqrt(d)
+    st.st_attn_spatial(to_dev(q), to_dev(k), to_dev(v), B, T, S, H, d, scale, dt, out)
+    sync()
+    ref = oracle.attn_spatial(f64(q), f64(k), f64(v), scale)
+    assert_close(f64(out), ref, bf16=dt == BF, what="O")
+
+
+TEMPORAL_CASES = [
+    # B, S, T, t_valid, H, d, dtype
+    (1, 37, 51, 51, 16, 72, BF),
+    (1, 20, 52, 51, 16, 72, BF),
+    (2, 10, 24, 24, 4, 72, BF),
+    (1, 5, 64, 60, 3, 72, BF),
+    (1, 3, 80, 70, 2, 72, BF),         # longer than the short kernel: long path
+    (1, 9, 1, 1, 2, 72, BF),           # T = 1
+    (1, 7, 33, 33, 2, 64, BF),
+    (1, 4, 20, 20, 2, 128, BF),        # d = 128: long path
+    (1, 64, 4, 4, 2, 64, F32),
+    (1, 6, 10, 7, 2, 64, F32),
+]
+
+
+@pytest.mark.parametrize("B,S,T,tv,H,d,dt", TEMPORAL_CASES)
+def test_attn_temporal(B, S, T, tv, H, d, dt):
+    q, k, v = qkv_tensors((B, S, T, H, d), 41 + T + S, dt)
+    out = empty((B, S, T, H, d), dt == BF)
+    scale = 1.0 / math.sqrt(d)
+    st.st_attn_temporal(to_dev(q), to_dev(k), to_dev(v), B, S, T, tv, H, d, scale, dt, out)
+    sync()
+    ref = oracle.attn_temporal(f64(q), f64(k), f64(v), scale, tv)
+    assert_close(f64(out), ref, bf16=dt == BF, what="O")
+
+
+def test_attention_is_deterministic():
+    q, k, v = qkv_tensors((1, 2, 500, 2, 72), 77, BF)
+    dq, dk, dv = to_dev(q), to_dev(k), to_dev(v)
+    outs = []
+    for _ in range(3):
+        o = empty((1, 2, 500, 2, 72))
+        st.st_attn_spatial(dq, dk, dv, 1, 2, 500, 2, 72, 1 / math.sqrt(72), BF, o)
+        outs.append(to_host(o))
+    sync()
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
