@@ -1,0 +1,232 @@
+"""Benchmark of the ST-DiT attention block on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1080p|720p] [--no-cpu] [--no-sliced]
+
+A step is one pass of the unsliced spatial + temporal layer pair over the
+1080p 8 s latent (B=1, T=51, S=8160 on a 120x68 patch grid, C=1152,
+16 heads x 72, bf16): QKV projection with RMSNorm and 2D RoPE, spatial
+attention, output projection, [B,T,S,C] -> [B,S,T,C] relayout, QKV
+projection with 1D RoPE, temporal attention, output projection, relayout
+back.  Inputs are seeded synthetic tensors already resident in HBM.
+
+The JSON line reports the whole-step throughput in algorithmic TFLOP/s, each
+kernel's average duration from HIP events recorded on the launch stream, a
+roofline entry for the dominant kernel (spatial attention), the slicing
+schedule's time (N_T = N_S = 4, T padded to 52), and the fp64 oracle timed
+on a bounded sample on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "ST-DiT attention block TFLOP/s + relayout GB/s (% of peak) at 1080p shape"
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+WORKLOADS = {"1080p": 3, "720p": 2}
+
+
+def flops_and_bytes(B, T, S, C, H, d):
+    N, hd = B * T * S, H * d
+    f = {
+        "qkv_spatial": 2.0 * N * C * 3 * hd,
+        "attn_spatial": 4.0 * S * S * d * H * B * T,
+        "proj_spatial": 2.0 * N * hd * C,
+        "qkv_temporal": 2.0 * N * C * 3 * hd,
+        "attn_temporal": 4.0 * T * T * d * H * B * S,
+        "proj_temporal": 2.0 * N * hd * C,
+    }
+    by = {
+        "relayout_fwd": 2.0 * N * C * 2,          # read + write every element once
+        "relayout_bwd": 2.0 * N * C * 2,
+        "attn_temporal": 4.0 * N * hd * 2,        # read q, k, v; write o
+    }
+    return f, by
+
+
+def cpu_baseline(inp, cfg, budget_s=20.0):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload.
+
+    Sample: the spatial layer on whole frames (all 16 heads, all 8160 patches),
+    one frame at a time until the time budget is reached, plus the temporal
+    layer on 160 patches x all frames.  Throughput = algorithmic flops of the
+    sample / wall time.
+    """
+    import oracle
+    import st_synth
+    from threadpoolctl import threadpool_info
+
+    B, T, S, C, H, d, gw = cfg["B"], cfg["T"], cfg["S"], cfg["C"], cfg["H"], cfg["d"], cfg["grid_w"]
+    eps, base = st_synth.EPS, st_synth.ROPE_BASE
+    ws = dict(w_qkv=st_synth.to_f64(inp["w_qkv_s"]), w_o=st_synth.to_f64(inp["w_o_s"]),
+              g_q=inp["g_q"].astype(np.float64), g_k=inp["g_k"].astype(np.float64))
+    wt = dict(w_qkv=st_synth.to_f64(inp["w_qkv_t"]), w_o=st_synth.to_f64(inp["w_o_t"]),
+              g_q=inp["g_q"].astype(np.float64), g_k=inp["g_k"].astype(np.float64))
+    hd = H * d
+    flops, frames = 0.0, 0
+    t0 = time.perf_counter()
+    while frames < T and time.perf_counter() - t0 < budget_s / 2:
+        x = st_synth.to_f64(inp["x"][:, frames:frames + 1])
+        oracle.spatial_layer(x, ws, H, d, gw, eps, base)
+        flops += 2.0 * S * C * 3 * hd + 4.0 * S * S * d * H + 2.0 * S * hd * C
+        frames += 1
+    P = 160
+    xt = oracle.bt_to_bs(st_synth.to_f64(inp["x"][:, :, :P]))
+    oracle.temporal_layer(xt, wt, H, d, eps, base)
+    flops += 2.0 * P * T * C * 3 * hd + 4.0 * T * T * d * H * P + 2.0 * P * T * hd * C
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"spatial layer on {frames} whole frame(s) (8160 patches x 16 heads) + temporal layer on "
+                      f"{P} patches x {T} frames; fp64 numpy, {dt:.1f} s wall",
+            "seconds": round(dt, 2), "host_cores_visible": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="1080p", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-sliced", action="store_true", help="skip timing the slicing schedule")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); multi-GPU runs are not part of this build",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import st_synth
+    import temporal_attention_amd as st
+    from temporal_attention_amd.pipeline import LayerPair
+
+    torch.cuda.set_device(0)
+    cfg_id = WORKLOADS[args.workload]
+    inp = st_synth.make_inputs(cfg_id)
+    cfg = inp["cfg"]
+    B, T, S, C, H, d, gw = cfg["B"], cfg["T"], cfg["S"], cfg["C"], cfg["H"], cfg["d"], cfg["grid_w"]
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+    x = dev(inp["x"])
+    wsd = dict(w_qkv=dev(inp["w_qkv_s"]), w_o=dev(inp["w_o_s"]), g_q=torch.from_numpy(inp["g_q"]).cuda(),
+               g_k=torch.from_numpy(inp["g_k"]).cuda())
+    wtd = dict(w_qkv=dev(inp["w_qkv_t"]), w_o=dev(inp["w_o_t"]), g_q=torch.from_numpy(inp["g_q"]).cuda(),
+               g_k=torch.from_numpy(inp["g_k"]).cuda())
+    lp = LayerPair(B, T, S, gw, C, H, d)
+    lp.set_weights(wsd, wtd)
+    steps = lp.steps(x)
+    names = [n for n, _ in steps]
+
+    for _ in range(args.warmup):
+        for _, fn in steps:
+            fn()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(steps) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        for j, (_, fn) in enumerate(steps):
+            fn()
+            ev[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {n: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
+           for j, n in enumerate(names)}
+    step_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][-1]) for i in range(args.steps)]))
+    ms_per_step = wall * 1e3 / args.steps   # bracketed by synchronize on both sides
+
+    fl, by = flops_and_bytes(B, T, S, C, H, d)
+    total_flops = sum(fl.values())
+    kernels = {}
+    for n in names:
+        e = {"ms": round(per[n], 4)}
+        if n in fl:
+            e["tflops"] = round(fl[n] / per[n] / 1e9, 1)
+            e["frac_mfma_peak"] = round(fl[n] / per[n] / 1e9 / PEAK_BF16_TFLOPS, 4)
+        if n in by:
+            e["gbs"] = round(by[n] / per[n] / 1e6, 1)
+            e["frac_hbm_peak"] = round(by[n] / per[n] / 1e6 / PEAK_HBM_GBS, 4)
+        kernels[n] = e
+    relayout_ms = per["relayout_fwd"] + per["relayout_bwd"]
+    relayout_gbs = (by["relayout_fwd"] + by["relayout_bwd"]) / relayout_ms / 1e6
+    attn_achieved = fl["attn_spatial"] / per["attn_spatial"] / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": round(total_flops / ms_per_step / 1e9, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_events": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg['name']} ST-DiT layer pair (spatial + temporal, both relayouts)", "B": B, "T": T,
+                   "S": S, "grid": f"{gw}x{S // gw}", "C": C, "heads": H, "head_dim": d,
+                   "step_tflop": round(total_flops / 1e12, 3)},
+        "block_tflops_excl_relayout": round(total_flops / (ms_per_step - relayout_ms) / 1e9, 2),
+        "relayout_gbs": round(relayout_gbs, 1),
+        "relayout_frac_hbm_peak": round(relayout_gbs / PEAK_HBM_GBS, 4),
+        "kernels": kernels,
+        "roofline": {"kernel": "attn_long_kernel<72,2> (spatial attention)", "bound": "mfma",
+                     "achieved": round(attn_achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+    }
+
+    if not args.no_sliced:
+        # the slicing schedule: T padded 51 -> 52 with a zero frame, N_T = N_S = 4
+        x4 = torch.cat([x.view(B, T, S, C), torch.zeros_like(x.view(B, T, S, C)[:, :1])], dim=1)
+        sp = st.layer_weights(wsd["w_qkv"], wsd["w_o"], wsd["g_q"], wsd["g_k"])
+        tp = st.layer_weights(wtd["w_qkv"], wtd["w_o"], wtd["g_q"], wtd["g_k"])
+        res = {}
+        for (nt, ns, TT, xx) in ((1, 1, T, x), (4, 4, T + 1, x4)):
+            nb = st.st_block_sliced_workspace(B, TT, S, gw, C, H, d, nt, ns, st.ST_BF16)
+            ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+            y = torch.empty((B, TT, S, C), dtype=torch.bfloat16, device="cuda")
+            run = lambda: st.st_block_sliced(xx, B, TT, T, S, gw, C, H, d, nt, ns, sp, tp, st_synth.EPS,  # noqa: E731
+                                             st_synth.ROPE_BASE, st.ST_BF16, y, ws, nb)
+            run()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = max(2, args.steps // 2)
+            e0.record(stream)
+            for _ in range(reps):
+                run()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            res[(nt, ns)] = (e0.elapsed_time(e1) / reps, y)
+            del ws
+        same = bool(torch.equal(res[(4, 4)][1][:, :T], res[(1, 1)][1]))
+        out["sliced"] = {"n_t": 4, "n_s": 4, "T_padded": T + 1, "ms": round(res[(4, 4)][0], 4),
+                         "unsliced_native_ms": round(res[(1, 1)][0], 4),
+                         "overhead": round(res[(4, 4)][0] / res[(1, 1)][0] - 1.0, 4),
+                         "bit_identical_to_unsliced": same}
+        del x4, res
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
