@@ -88,11 +88,20 @@ __device__ __forceinline__ bf16x8 pack_p(const f32x16 &s, int base) {
 }
 
 __device__ __forceinline__ float max16(const f32x16 &s) {
-  float m0 = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-  float m1 = fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7]));
-  float m2 = fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11]));
-  float m3 = fmaxf(fmaxf(s[12], s[13]), fmaxf(s[14], s[15]));
-  return fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
+  float m = __builtin_fmaxf(__builtin_fmaxf(s[0], s[1]), s[2]);
+#pragma unroll
+  for (int i = 3; i < 15; i += 2) m = __builtin_fmaxf(__builtin_fmaxf(m, s[i]), s[i + 1]);
+  return __builtin_fmaxf(m, s[15]);
+}
+
+// max(x[l], x[l ^ 32]): the two half-waves hold the two halves of a query's keys.
+// v_permlane32_swap exchanges lanes 32..63 of its first operand with lanes
+// 0..31 of its second, so with both operands = x the two results hold x and
+// its partner in some order, and their max is the same in every lane.
+__device__ __forceinline__ float max_across_halves(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // Key index (within a 32-key tile) of accumulator register r in lane half g.
@@ -106,19 +115,157 @@ constexpr float kRescale = 8.0f;   // log2 growth of the running max that forces
 template <int D, int NT>
 struct LongCfg {
   typedef Dims<D> DM;
-  static constexpr int KB = 64;                  // keys per LDS tile
-  static constexpr int QW = 32 * NT;             // queries per wave
-  static constexpr int QB = 4 * QW;              // queries per workgroup
-  static constexpr int K_LD = DM::DQK + 8;       // LDS row stride of K (u16)
-  static constexpr int V_LD = KB + 4;            // LDS row stride of V^T (u16)
-  static constexpr int K_TILE = KB * K_LD;
-  static constexpr int V_TILE = DM::DV * V_LD;
-  static constexpr int STAGE = K_TILE + V_TILE;
-  static constexpr int K_CHUNKS = KB * DM::CH;
-  static constexpr int K_PER_T = (K_CHUNKS + 255) / 256;
-  static constexpr int V_TASKS = (KB / 4) * DM::CH;   // (4 keys x 8 dims) per task
-  static constexpr int V_PER_T = (V_TASKS + 255) / 256;
+  static constexpr int KB = 64;                   // keys per LDS tile
+  static constexpr int QW = 32 * NT;              // queries per wave
+  static constexpr int QB = 4 * QW;               // queries per workgroup
+  static constexpr int TILE = KB * D;             // u16 per K or V tile: rows packed as in memory
+  static constexpr int SLACK = 32;                // u16 after a tile: operand reads run past the last row
+  static constexpr int REGION = TILE + SLACK;
+  static constexpr int STAGE = 2 * REGION;        // K tile, then V tile
+  static constexpr int BLOCKS = TILE * 2 / 1024;  // 1 KB direct-to-LDS loads per tile
+  static_assert((TILE * 2) % 1024 == 0, "tile must be whole 1 KB blocks");
 };
+
+// Wait until this wave's outstanding global->LDS loads have landed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
+
+// K and V tiles go global -> LDS directly, 1 KB per wavefront instruction:
+// lane l of block b carries 16-byte chunk 64 b + l of the packed [key][d]
+// tile.  The 2 * BLOCKS blocks of a stage are dealt round-robin to the four
+// waves; each lane's element offset inside a tile (key * row stride + dim) is
+// fixed for the whole key loop, so it is computed once.  Keys past L repeat
+// row L-1 (their scores are masked).
+template <int D>
+struct LongDma {
+  typedef LongCfg<D, 1> C;
+  static constexpr int PER_WAVE = (2 * C::BLOCKS + 3) / 4;
+  int off[PER_WAVE];   // element offset of this lane's chunk within a tile
+  int key[PER_WAVE];   // key of this lane's chunk within a tile
+
+  __device__ __forceinline__ void init(int64_t rs, int lane, int wave) {
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int n = wave + 4 * i;
+      const int b = n >= C::BLOCKS ? n - C::BLOCKS : n;
+      const int c = b * 64 + lane;
+      key[i] = c / Dims<D>::CH;
+      off[i] = (int)(key[i] * rs) + (c % Dims<D>::CH) * 8;
+    }
+  }
+
+  __device__ __forceinline__ void issue(u16 *__restrict__ dst_stage, int kb, const u16 *kp, const u16 *vp, int64_t rs,
+                                        int L, int wave) const {
+    const bool tail = kb + C::KB > L;
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int n = wave + 4 * i;
+      if (n < 2 * C::BLOCKS) {
+        const bool isv = n >= C::BLOCKS;
+        const int b = isv ? n - C::BLOCKS : n;
+        const u16 *base = (isv ? vp : kp) + (int64_t)kb * rs;
+        int o = off[i];
+        if (tail && kb + key[i] >= L) o += (int)((L - 1 - kb - key[i]) * rs);   // repeat row L-1
+        u16 *dst = dst_stage + (isv ? C::REGION : 0) + b * 512;
+        __builtin_amdgcn_global_load_lds(base + o, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+      }
+    }
+  }
+};
+
+// One 64-key tile for one wave: issue the next tile's loads into `nxt`, then
+// S^T = K Q^T, online softmax, O^T += V^T P^T on the tile in Ks / Vs.  The
+// three stage pointers are restrict-qualified: the next tile's loads never
+// alias the tile being read.
+template <int D, int NT>
+__device__ __forceinline__ void long_tile(const u16 *__restrict__ Ks, const u16 *__restrict__ Vs,
+                                          u16 *__restrict__ nxt, bool prefetch, int kt, const AttnArgs &a,
+                                          const LongDma<D> &dma, const u16 *kp, const u16 *vp, int64_t rs, int L,
+                                          int nv, int lane, int g,
+                                          int l32, int wave, int v_off, bool vkeep, uint32_t vconst,
+                                          const bf16x8 (&qf)[NT][Dims<D>::KS], f32x16 (&oacc)[Dims<D>::DT][NT],
+                                          float (&mref)[NT], float (&lsum)[NT]) {
+  typedef LongCfg<D, NT> C;
+  typedef Dims<D> DM;
+  if (prefetch) dma.issue(nxt, (kt + 1) * C::KB, kp, vp, rs, L, wave);
+  const int kb = kt * C::KB;
+  const bool masked = kb + C::KB > nv;
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub) {
+    f32x16 s[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[nt][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < DM::KS; ++ks) {
+      const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(Ks + (sub * 32 + l32) * D + ks * 16 + g * 8);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) s[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[nt][ks], s[nt], 0, 0, 0);
+    }
+    if (masked) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const bool off = kb + sub * 32 + acc_row(r, g) >= nv;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) s[nt][r] = off ? -INFINITY : s[nt][r];
+      }
+    }
+    float mx[NT];
+    bool grow = false;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      mx[nt] = max_across_halves(max16(s[nt]));
+      grow |= (mx[nt] - mref[nt]) * a.c > kRescale;
+    }
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const float mnew = fmaxf(mref[nt], mx[nt]);
+        const float alpha = __builtin_amdgcn_exp2f((mref[nt] - mnew) * a.c);
+        mref[nt] = mnew;
+        lsum[nt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DM::DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[dt][nt][r] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const float mc = mref[nt] * a.c;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[nt][r] = __builtin_amdgcn_exp2f(fmaf(s[nt][r], a.c, -mc));
+      if constexpr (!DM::ONES) {
+        float acc = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc += s[nt][r];
+        lsum[nt] += acc;
+      }
+    }
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      bf16x8 pf[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) pf[nt] = pack_p(s[nt], ks2 * 8);
+      const u16 *vb = Vs + (sub * 32 + ks2 * 16) * D + v_off;
+#pragma unroll
+      for (int dt = 0; dt < DM::DT; ++dt) {
+        typedef short v4s __attribute__((ext_vector_type(4)));
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s *)(vb + dt * 32));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s *)(vb + dt * 32 + 8 * D));
+        uint4 u = make_uint4(__builtin_bit_cast(uint2, lo).x, __builtin_bit_cast(uint2, lo).y,
+                             __builtin_bit_cast(uint2, hi).x, __builtin_bit_cast(uint2, hi).y);
+        if (DM::DV != D && dt == DM::DT - 1 && !vkeep) u = make_uint4(vconst, vconst, vconst, vconst);
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, u);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          oacc[dt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[nt], oacc[dt][nt], 0, 0, 0);
+      }
+    }
+  }
+}
 
 template <int D, int NT>
 __global__ void __launch_bounds__(256, 2) attn_long_kernel(AttnArgs a, uint32_t nqb, uint32_t nblocks) {
@@ -141,18 +288,9 @@ __global__ void __launch_bounds__(256, 2) attn_long_kernel(AttnArgs a, uint32_t 
   const int l32 = lane & 31, g = lane >> 5;
   const int L = a.L, nv = a.n_valid;
 
-  // Constant parts of both stages: K pad columns [D, DQK) = 0; V^T rows [D, DV) = 0,
-  // except the ones row.
-  for (int i = t; i < 2 * C::KB; i += 256) {
-    u16 *row = lds + (i / C::KB) * C::STAGE + (i % C::KB) * C::K_LD;
-    for (int dd = D; dd < DM::DQK; ++dd) row[dd] = 0;
-  }
-  for (int i = t; i < 2 * (DM::DV - D) * C::V_LD; i += 256) {
-    const int st = i / ((DM::DV - D) * C::V_LD);
-    const int rem = i % ((DM::DV - D) * C::V_LD);
-    const int dd = D + rem / C::V_LD;
-    lds[st * C::STAGE + C::K_TILE + dd * C::V_LD + rem % C::V_LD] = (DM::ONES && dd == D) ? (u16)0x3F80 : (u16)0;
-  }
+  // Slack after every tile is zero, so operand reads that run past the last
+  // row multiply finite values by the zero padding of Q (K) or get replaced (V).
+  for (int i = t; i < 4 * C::SLACK; i += 256) lds[(i / C::SLACK) * C::REGION + C::TILE + i % C::SLACK] = 0;
 
   // Q operand fragments (B of S^T = K Q^T), held for the whole key loop.
   const int q0 = qb * C::QB + wave * C::QW;
@@ -183,138 +321,32 @@ __global__ void __launch_bounds__(256, 2) attn_long_kernel(AttnArgs a, uint32_t 
     lsum[j] = 0.f;
   }
 
+  // V^T operand via LDS transpose reads (ds_read_b64_tr_b16): in each 16-lane
+  // group, lane i receives element (i & 3) of the 8 bytes addressed by lanes
+  // 4j + (i >> 2), j = 0..3.  Lane 4j + q of group G addresses V[key0 + j][dg + 4q]
+  // with dg = 32 dt + 16 (G & 1), so lane i of the group gets 4 consecutive keys
+  // of dimension dg + i: exactly the A-operand layout (row = lane % 32).
+  const int grp = lane >> 4, gi = lane & 15;
+  const int v_off = (gi >> 2) * D + 16 * (grp & 1) + 4 * (gi & 3) + 4 * (grp >> 1) * D;
+  // rows past D in the last P.V tile: the ones row, then zeros
+  const int dlast = 32 * (DM::DT - 1) + l32;
+  const bool vkeep = dlast < D;
+  const uint32_t vconst = (DM::ONES && dlast == D) ? 0x3F803F80u : 0u;
+
   const int nkt = (min(L, nv) + C::KB - 1) / C::KB;   // tiles past n_valid carry no weight
-  uint4 rk[C::K_PER_T], rv[C::V_PER_T][4];
-
-  auto gload = [&](int kt) {
-    const int kb = kt * C::KB;
-#pragma unroll
-    for (int i = 0; i < C::K_PER_T; ++i) {
-      const int c = t + 256 * i;
-      const int key = c / DM::CH, ch = c % DM::CH;
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (c < C::K_CHUNKS && kb + key < L) u = *reinterpret_cast<const uint4 *>(kp + (int64_t)(kb + key) * rs + ch * 8);
-      rk[i] = u;
-    }
-#pragma unroll
-    for (int i = 0; i < C::V_PER_T; ++i) {
-      const int task = t + 256 * i;
-      const int key4 = task % (C::KB / 4), ch = task / (C::KB / 4);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = kb + key4 * 4 + j;
-        uint4 u = make_uint4(0, 0, 0, 0);
-        if (task < C::V_TASKS && key < L) u = *reinterpret_cast<const uint4 *>(vp + (int64_t)key * rs + ch * 8);
-        rv[i][j] = u;
-      }
-    }
-  };
-  auto sstore = [&](int stage) {
-    u16 *Ks = lds + stage * C::STAGE;
-    u16 *Vs = Ks + C::K_TILE;
-#pragma unroll
-    for (int i = 0; i < C::K_PER_T; ++i) {
-      const int c = t + 256 * i;
-      if (c < C::K_CHUNKS) *reinterpret_cast<uint4 *>(Ks + (c / DM::CH) * C::K_LD + (c % DM::CH) * 8) = rk[i];
-    }
-#pragma unroll
-    for (int i = 0; i < C::V_PER_T; ++i) {
-      const int task = t + 256 * i;
-      if (task < C::V_TASKS) {
-        const int key4 = task % (C::KB / 4), ch = task / (C::KB / 4);
-        uint2 tr[8];
-        transpose4x8(rv[i], tr);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) *reinterpret_cast<uint2 *>(Vs + (ch * 8 + j) * C::V_LD + key4 * 4) = tr[j];
-      }
-    }
-  };
-
-  if (nkt > 0) {
-    gload(0);
-    sstore(0);
-  }
+  LongDma<D> dma;
+  dma.init(rs, lane, wave);
+  if (nkt > 0) dma.issue(lds, 0, kp, vp, rs, L, wave);
+  wait_vmem();
   __syncthreads();
 
   for (int kt = 0; kt < nkt; ++kt) {
     const int stage = kt & 1;
-    if (kt + 1 < nkt) gload(kt + 1);
-    const u16 *Ks = lds + stage * C::STAGE;
-    const u16 *Vs = Ks + C::K_TILE;
-    const int kb = kt * C::KB;
-    const bool masked = kb + C::KB > nv;
-
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      f32x16 s[NT];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[nt][r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < DM::KS; ++ks) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(Ks + (sub * 32 + l32) * C::K_LD + ks * 16 + g * 8);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) s[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[nt][ks], s[nt], 0, 0, 0);
-      }
-      if (masked) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const bool off = kb + sub * 32 + acc_row(r, g) >= nv;
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) s[nt][r] = off ? -INFINITY : s[nt][r];
-        }
-      }
-      float mx[NT];
-      bool grow = false;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        mx[nt] = max16(s[nt]);
-        mx[nt] = fmaxf(mx[nt], __shfl_xor(mx[nt], 32));
-        grow |= (mx[nt] - mref[nt]) * a.c > kRescale;
-      }
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const float mnew = fmaxf(mref[nt], mx[nt]);
-          const float alpha = __builtin_amdgcn_exp2f((mref[nt] - mnew) * a.c);
-          mref[nt] = mnew;
-          lsum[nt] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < DM::DT; ++dt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[dt][nt][r] *= alpha;
-        }
-      }
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const float mc = mref[nt] * a.c;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[nt][r] = __builtin_amdgcn_exp2f(fmaf(s[nt][r], a.c, -mc));
-        if constexpr (!DM::ONES) {
-          float acc = 0.f;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc += s[nt][r];
-          lsum[nt] += acc;
-        }
-      }
-#pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2) {
-        bf16x8 pf[NT];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) pf[nt] = pack_p(s[nt], ks2 * 8);
-        const int kk = sub * 32 + ks2 * 16 + g * 4;
-#pragma unroll
-        for (int dt = 0; dt < DM::DT; ++dt) {
-          const u16 *vrow = Vs + (dt * 32 + l32) * C::V_LD + kk;
-          const bf16x8 vf = as_bf16x8(*reinterpret_cast<const uint2 *>(vrow), *reinterpret_cast<const uint2 *>(vrow + 8));
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
-            oacc[dt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[nt], oacc[dt][nt], 0, 0, 0);
-        }
-      }
-    }
-    if (kt + 1 < nkt) sstore(stage ^ 1);
+    u16 *cur = lds + stage * C::STAGE;
+    u16 *nxt = lds + (stage ^ 1) * C::STAGE;
+    long_tile<D, NT>(cur, cur + C::REGION, nxt, kt + 1 < nkt, kt, a, dma, kp, vp, rs, L, nv, lane, g, l32, wave, v_off,
+                     vkeep, vconst, qf, oacc, mref, lsum);
+    wait_vmem();
     __syncthreads();
   }
 
@@ -441,7 +473,7 @@ __global__ void __launch_bounds__(256, 2) attn_short_kernel(AttnArgs a, uint32_t
           s[mt][nt][r] = x;
           mx = fmaxf(mx, x);
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = max_across_halves(mx);
       const float mc = mx * a.c;
 #pragma unroll
       for (int mt = 0; mt < NT; ++mt)
