@@ -103,7 +103,7 @@ st_status st_rope_table(int d, int kind, float base, int n_pos, float *table, vo
  *   H, d          heads and head dim; dtype ST_BF16 supports d in {64, 72, 128},
  *                 ST_F32 supports even d <= 128 (multiple of 4 for 2D RoPE).
  *   q, k, v  out  [rows, H, d]           (dtype)
- * c_in must be a multiple of 8.  rows may be 0 (no work).
+ * bf16: c_in must be a multiple of 64 (the K step of the MFMA pipeline).  rows may be 0 (no work).
  */
 st_status st_qkv_norm_rope(const void *x, int64_t rows, int c_in, const void *w_qkv,
                            const float *g_q, const float *g_k, float eps,
@@ -117,7 +117,7 @@ st_status st_qkv_norm_rope(const void *x, int64_t rows, int c_in, const void *w_
  * as projection -> norm/RoPE -> attention -> output projection.
  *
  *   a  in  [rows, k_in]   w in [n_out, k_in]   y out [rows, n_out]   (dtype)
- * k_in must be a multiple of 8, n_out a multiple of 4.
+ * bf16: k_in must be a multiple of 64.  n_out must be a multiple of 4.
  */
 st_status st_out_proj(const void *a, int64_t rows, int k_in, const void *w, int n_out,
                       int dtype, void *y, void *stream);
@@ -189,7 +189,8 @@ typedef struct {
  * masked); the result is rearranged back to y [B, T, S, C].
  * n_t = n_s = 1 is the unsliced layer pair.
  *
- *   x         in   [B, T, S, C]   T % n_t == 0, S % n_s == 0 (the caller pads T
+ *   x         in   [B, T, S, C]   bf16: C and H*d multiples of 64.
+ *                                 T % n_t == 0, S % n_s == 0 (the caller pads T
  *                                 with zero frames and passes t_valid)
  *   grid_w         patch-grid width; S % grid_w == 0; s = h * grid_w + w
  *   spatial, temporal   host pointers to the two layers' weights

@@ -108,16 +108,24 @@ __device__ __forceinline__ float max_across_halves(float x) {
 __device__ __forceinline__ int acc_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
 
 constexpr float kRescale = 8.0f;   // log2 growth of the running max that forces a rescale
+#ifndef ST_LONG_WAVES
+#define ST_LONG_WAVES 8
+#endif
+// Waves per workgroup of the long kernel: every workgroup streams all keys of
+// its sequence through LDS, so more queries per workgroup means less L2->LDS
+// traffic per flop.
+constexpr int kLongWaves = ST_LONG_WAVES;
 
 // ------------------------------------------------------------------------- //
 // Long sequences                                                            //
 // ------------------------------------------------------------------------- //
-template <int D, int NT>
+template <int D, int NT, int W = kLongWaves>
 struct LongCfg {
   typedef Dims<D> DM;
+  static constexpr int WAVES = W;                 // waves per workgroup
   static constexpr int KB = 64;                   // keys per LDS tile
   static constexpr int QW = 32 * NT;              // queries per wave
-  static constexpr int QB = 4 * QW;               // queries per workgroup
+  static constexpr int QB = WAVES * QW;           // queries per workgroup
   static constexpr int TILE = KB * D;             // u16 per K or V tile: rows packed as in memory
   static constexpr int SLACK = 32;                // u16 after a tile: operand reads run past the last row
   static constexpr int REGION = TILE + SLACK;
@@ -138,14 +146,14 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
 template <int D>
 struct LongDma {
   typedef LongCfg<D, 1> C;
-  static constexpr int PER_WAVE = (2 * C::BLOCKS + 3) / 4;
+  static constexpr int PER_WAVE = (2 * C::BLOCKS + C::WAVES - 1) / C::WAVES;
   int off[PER_WAVE];   // element offset of this lane's chunk within a tile
   int key[PER_WAVE];   // key of this lane's chunk within a tile
 
   __device__ __forceinline__ void init(int64_t rs, int lane, int wave) {
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
-      const int n = wave + 4 * i;
+      const int n = wave + C::WAVES * i;
       const int b = n >= C::BLOCKS ? n - C::BLOCKS : n;
       const int c = b * 64 + lane;
       key[i] = c / Dims<D>::CH;
@@ -158,7 +166,7 @@ struct LongDma {
     const bool tail = kb + C::KB > L;
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
-      const int n = wave + 4 * i;
+      const int n = wave + C::WAVES * i;
       if (n < 2 * C::BLOCKS) {
         const bool isv = n >= C::BLOCKS;
         const int b = isv ? n - C::BLOCKS : n;
@@ -268,7 +276,8 @@ __device__ __forceinline__ void long_tile(const u16 *__restrict__ Ks, const u16 
 }
 
 template <int D, int NT>
-__global__ void __launch_bounds__(256, 2) attn_long_kernel(AttnArgs a, uint32_t nqb, uint32_t nblocks) {
+__global__ void __launch_bounds__(64 * kLongWaves, 8 / kLongWaves) attn_long_kernel(AttnArgs a, uint32_t nqb,
+                                                                                  uint32_t nblocks) {
   typedef LongCfg<D, NT> C;
   typedef Dims<D> DM;
   __shared__ __attribute__((aligned(16))) u16 lds[2 * C::STAGE];
@@ -290,7 +299,7 @@ __global__ void __launch_bounds__(256, 2) attn_long_kernel(AttnArgs a, uint32_t 
 
   // Slack after every tile is zero, so operand reads that run past the last
   // row multiply finite values by the zero padding of Q (K) or get replaced (V).
-  for (int i = t; i < 4 * C::SLACK; i += 256) lds[(i / C::SLACK) * C::REGION + C::TILE + i % C::SLACK] = 0;
+  for (int i = t; i < 4 * C::SLACK; i += 64 * C::WAVES) lds[(i / C::SLACK) * C::REGION + C::TILE + i % C::SLACK] = 0;
 
   // Q operand fragments (B of S^T = K Q^T), held for the whole key loop.
   const int q0 = qb * C::QB + wave * C::QW;
@@ -559,7 +568,7 @@ st_status launch_long(const AttnArgs &a, hipStream_t s) {
   const int64_t nqb = (a.L + C::QB - 1) / C::QB;
   const int64_t nb = nqb * a.outer * a.H;
   if (nb >= (1ll << 31)) return ST_EUNSUPPORTED;
-  hipLaunchKernelGGL((attn_long_kernel<D, NT>), dim3((uint32_t)nb), dim3(256), 0, s, a, (uint32_t)nqb,
+  hipLaunchKernelGGL((attn_long_kernel<D, NT>), dim3((uint32_t)nb), dim3(64 * C::WAVES), 0, s, a, (uint32_t)nqb,
                      (uint32_t)nb);
   return launch_status();
 }

@@ -15,9 +15,12 @@
 // whole heads, so the epilogue runs on the fp32 accumulator and stores bf16
 // once: the norm and RoPE cost no extra HBM traffic.
 //
-// Tiling: 4 waves as 2 (channels) x 2 (tokens); a wave owns 16*CT channels x
-// 64 tokens (CT*4 accumulator tiles).  K advances 32 per step through a
-// double-buffered LDS stage fed by register prefetch, one barrier per step.
+// Tiling: 8 waves as 2 (channels) x 4 (tokens); a wave owns 16*CT channels x
+// 64 tokens (CT*4 accumulator tiles), a workgroup 32*CT channels x 256 tokens.
+// Both operands reach LDS by direct global->LDS loads, K advancing 64 per step
+// (whole 128-byte lines of both operands) through two LDS stages.  Moving
+// operands from L2 into LDS, not the MFMAs, bounds this kernel, so the tile is
+// as large as the LDS allows and every load instruction covers whole lines.
 // The grid is remapped so the channel tiles of one token block run on the same
 // XCD and share its L2 copy of the activations.
 #include "st_internal.h"
@@ -25,10 +28,21 @@
 namespace st {
 namespace {
 
-constexpr int kBK = 32;          // K per pipeline step
-constexpr int kLdsK = kBK + 8;   // padded LDS row (80 B): conflict-free 16 B reads
-constexpr int kWM = 64;          // tokens per wave
-constexpr int kBM = 2 * kWM;     // tokens per workgroup
+constexpr int kBK = 64;          // K per pipeline step (128-byte rows in LDS)
+constexpr int kTT = 4;           // 16-token MFMA tiles per wave
+constexpr int kWM = 16 * kTT;    // tokens per wave
+constexpr int kWavesM = 4;        // token-direction waves per workgroup
+constexpr int kThreads = 64 * 2 * kWavesM;
+constexpr int kBM = kWavesM * kWM;  // tokens per workgroup
+constexpr int kStages = 2;       // LDS pipeline depth
+constexpr uint32_t kGroupN = 16; // channel tiles sharing a token-block sweep
+
+// s_waitcnt vmcnt(N): at most N of this wave's vector-memory operations outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmem_upto() {
+  static_assert(N < 64, "vmcnt field is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
 
 struct GemmArgs {
   const u16 *x;      // [M, K]
@@ -47,110 +61,132 @@ struct GemmArgs {
 
 template <int CT>
 struct Tile {
-  static constexpr int WN = 16 * CT;   // channels per wave
-  static constexpr int BN = 2 * WN;    // channels per workgroup
-  static constexpr int A_CHUNKS = BN * kBK / 8;
-  static constexpr int B_CHUNKS = kBM * kBK / 8;
-  static constexpr int A_PER_T = (A_CHUNKS + 255) / 256;
-  static constexpr int B_PER_T = (B_CHUNKS + 255) / 256;
-  static constexpr int LDS_A = BN * kLdsK;   // u16 elements per stage
-  static constexpr int LDS_B = kBM * kLdsK;
+  static constexpr int WN = 16 * CT;                 // channels per wave
+  static constexpr int BN = 2 * WN;                  // channels per workgroup
+  static constexpr int LDS_A = BN * kBK;             // u16 per stage: W rows
+  static constexpr int LDS_B = kBM * kBK;            // u16 per stage: X rows
+  static constexpr int STAGE = LDS_A + LDS_B;
+  static constexpr int A_BLOCKS = LDS_A * 2 / 1024;  // 1 KB direct-to-LDS loads per stage
+  static constexpr int B_BLOCKS = LDS_B * 2 / 1024;
+  static constexpr int BLOCKS = A_BLOCKS + B_BLOCKS;
+  static constexpr int NWAVES = kThreads / 64;
+  static constexpr int PER_WAVE = (BLOCKS + NWAVES - 1) / NWAVES;
+  static_assert(LDS_A * 2 % 1024 == 0 && LDS_B * 2 % 1024 == 0, "stage must be whole 1 KB blocks");
 };
 
-template <int CT>
-__device__ __forceinline__ void load_stage(const GemmArgs &a, int64_t m0, int n0, int k0, uint4 (&ra)[Tile<CT>::A_PER_T],
-                                           uint4 (&rb)[Tile<CT>::B_PER_T]) {
-  typedef Tile<CT> TL;
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < TL::A_PER_T; ++i) {
-    const int c = t + 256 * i;
-    const int row = c >> 2, kc = (c & 3) * 8;
-    const int n = n0 + row, kk = k0 + kc;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (c < TL::A_CHUNKS && n < a.N && kk < a.K) val = *reinterpret_cast<const uint4 *>(a.w + (int64_t)n * a.K + kk);
-    ra[i] = val;
-  }
-#pragma unroll
-  for (int i = 0; i < TL::B_PER_T; ++i) {
-    const int c = t + 256 * i;
-    const int row = c >> 2, kc = (c & 3) * 8;
-    const int64_t m = m0 + row;
-    const int kk = k0 + kc;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (c < TL::B_CHUNKS && m < a.M && kk < a.K) val = *reinterpret_cast<const uint4 *>(a.x + m * a.K + kk);
-    rb[i] = val;
-  }
-}
+// LDS layout of a stage: rows of 64 bf16 (eight 16-byte chunks); chunk kc of row
+// r sits in slot r*8 + (kc ^ (r & 7)), so the 16-byte operand reads of 8
+// consecutive rows at one kc hit 8 disjoint bank quads.
+__device__ __forceinline__ int slot_of(int row, int kc) { return row * 8 + (kc ^ (row & 7)); }
 
+// Global -> LDS loads of one stage: 1 KB (8 whole rows) per wavefront
+// instruction, lane l of block b filling slot 64 b + l.  Each lane's element offset inside the K
+// window is fixed for the whole K loop and computed once; rows past M or N
+// repeat the last row (their results are never stored).
 template <int CT>
-__device__ __forceinline__ void store_stage(u16 *As, u16 *Bs, const uint4 (&ra)[Tile<CT>::A_PER_T],
-                                            const uint4 (&rb)[Tile<CT>::B_PER_T]) {
+struct GemmDma {
   typedef Tile<CT> TL;
-  const int t = threadIdx.x;
+  int off[TL::PER_WAVE];
+
+  __device__ __forceinline__ void init(const GemmArgs &a, int64_t m0, int n0, int lane, int wave) {
 #pragma unroll
-  for (int i = 0; i < TL::A_PER_T; ++i) {
-    const int c = t + 256 * i;
-    if (c < TL::A_CHUNKS) *reinterpret_cast<uint4 *>(As + (c >> 2) * kLdsK + (c & 3) * 8) = ra[i];
+    for (int i = 0; i < TL::PER_WAVE; ++i) {
+      const int n = wave + TL::NWAVES * i;
+      const bool isb = n >= TL::A_BLOCKS;
+      const int sl = (isb ? n - TL::A_BLOCKS : n) * 64 + lane;
+      const int row = sl >> 3;
+      const int kc = (sl & 7) ^ (row & 7);
+      const int r = isb ? (int)(min<int64_t>(m0 + row, a.M - 1) - m0) : min(n0 + row, a.N - 1);
+      off[i] = r * a.K + 8 * kc;
+    }
   }
+
+  __device__ __forceinline__ void issue(u16 *__restrict__ stage, int k0, const u16 *xb, const u16 *w, int wave) const {
 #pragma unroll
-  for (int i = 0; i < TL::B_PER_T; ++i) {
-    const int c = t + 256 * i;
-    if (c < TL::B_CHUNKS) *reinterpret_cast<uint4 *>(Bs + (c >> 2) * kLdsK + (c & 3) * 8) = rb[i];
+    for (int i = 0; i < TL::PER_WAVE; ++i) {
+      const int n = wave + TL::NWAVES * i;
+      if (n < TL::BLOCKS) {
+        const bool isb = n >= TL::A_BLOCKS;
+        const int b = isb ? n - TL::A_BLOCKS : n;
+        const u16 *src = (isb ? xb : w) + off[i] + k0;
+        u16 *dst = stage + (isb ? TL::LDS_A : 0) + b * 512;
+        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+      }
+    }
+  }
+};
+
+// One K step for one wave: issue the next step's loads into `nxt`, then
+// 2 x CT x 4 MFMAs on the stage in As / Bs.  Stage pointers are restrict-qualified:
+// the loads in flight never alias the stage being read.
+template <int CT>
+__device__ __forceinline__ void gemm_step(const u16 *__restrict__ As, const u16 *__restrict__ Bs,
+                                          u16 *__restrict__ nxt, bool prefetch, int k_next, const GemmDma<CT> &dma,
+                                          const u16 *xb, const u16 *w, int wave, int wn, int wm, int l16, int g4,
+                                          f32x4 (&acc)[CT][kTT]) {
+  typedef Tile<CT> TL;
+  if (prefetch) dma.issue(nxt, k_next, xb, w, wave);
+#pragma unroll
+  for (int ks = 0; ks < kBK / 32; ++ks) {
+    bf16x8 bf[kTT];
+#pragma unroll
+    for (int tt = 0; tt < kTT; ++tt)
+      bf[tt] = *reinterpret_cast<const bf16x8 *>(Bs + slot_of(wm * kWM + tt * 16 + l16, ks * 4 + g4) * 8);
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const bf16x8 af = *reinterpret_cast<const bf16x8 *>(As + slot_of(wn * TL::WN + ct * 16 + l16, ks * 4 + g4) * 8);
+#pragma unroll
+      for (int tt = 0; tt < kTT; ++tt)
+        acc[ct][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[tt], acc[ct][tt], 0, 0, 0);
+    }
   }
 }
 
 template <int CT, int D>
-__device__ __forceinline__ void epilogue_qkv(const GemmArgs &a, f32x4 (&acc)[CT][4], int64_t m0, int nw0, int wm,
+__device__ __forceinline__ void epilogue_qkv(const GemmArgs &a, f32x4 (&acc)[CT][kTT], int64_t m0, int nw0, int wm,
                                              int l16, int g4);
 
 // MODE 0: plain output y.  MODE 1: q/k/v with RMSNorm + RoPE on q, k (head dim D).
 template <int CT, int MODE, int D>
-__global__ void __launch_bounds__(256, 2) gemm_bf16_kernel(GemmArgs a, uint32_t n_tiles_n, uint32_t nblocks) {
+__global__ void __launch_bounds__(kThreads, 1) gemm_bf16_kernel(GemmArgs a, uint32_t n_tiles_n, uint32_t nblocks) {
   typedef Tile<CT> TL;
-  __shared__ __attribute__((aligned(16))) u16 lds[2 * (TL::LDS_A + TL::LDS_B)];
+  __shared__ __attribute__((aligned(16))) u16 lds[kStages * TL::STAGE];
 
+  // Tile order: channel tiles in groups of kGroupN, token blocks running
+  // fastest inside a group, and each XCD taking a contiguous range of that
+  // order.  An XCD then streams activations past a ~2.6 MB slice of W that
+  // stays in its L2, instead of cycling through all of W per token block.
   const uint32_t tile = xcd_remap(blockIdx.x, nblocks);
-  const int64_t m0 = (int64_t)(tile / n_tiles_n) * kBM;
-  const int n0 = (int)(tile % n_tiles_n) * TL::BN;
+  const uint32_t n_tiles_m = nblocks / n_tiles_n;
+  const uint32_t grp = tile / (kGroupN * n_tiles_m);
+  const uint32_t gsz = min(kGroupN, n_tiles_n - grp * kGroupN);
+  const uint32_t rem = tile - grp * kGroupN * n_tiles_m;
+  const int64_t m0 = (int64_t)(rem / gsz) * kBM;
+  const int n0 = (int)(grp * kGroupN + rem % gsz) * TL::BN;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int wn = wave & 1, wm = wave >> 1;
+  const int wn = wave & 1, wm = wave >> 1;   // 2 channel waves x kWavesM token waves
   const int l16 = lane & 15, g4 = lane >> 4;
 
-  f32x4 acc[CT][4];
+  f32x4 acc[CT][kTT];
 #pragma unroll
   for (int i = 0; i < CT; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < kTT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  uint4 ra[TL::A_PER_T], rb[TL::B_PER_T];
-  const int nk = (a.K + kBK - 1) / kBK;
-  load_stage<CT>(a, m0, n0, 0, ra, rb);
-  store_stage<CT>(lds, lds + TL::LDS_A, ra, rb);
+  GemmDma<CT> dma;
+  dma.init(a, m0, n0, lane, wave);
+  const u16 *xb = a.x + m0 * a.K;
+  const int nk = a.K / kBK;
+  dma.issue(lds, 0, xb, a.w, wave);
+  wait_vmem_upto<0>();
   __syncthreads();
-
   for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) load_stage<CT>(a, m0, n0, (kt + 1) * kBK, ra, rb);
-    const u16 *As = lds + buf * (TL::LDS_A + TL::LDS_B);
-    const u16 *Bs = As + TL::LDS_A;
-    bf16x8 bf[4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-      bf[tt] = *reinterpret_cast<const bf16x8 *>(Bs + (wm * kWM + tt * 16 + l16) * kLdsK + g4 * 8);
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      const bf16x8 af = *reinterpret_cast<const bf16x8 *>(As + (wn * TL::WN + ct * 16 + l16) * kLdsK + g4 * 8);
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-        acc[ct][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[tt], acc[ct][tt], 0, 0, 0);
-    }
-    if (kt + 1 < nk) {
-      u16 *An = lds + (buf ^ 1) * (TL::LDS_A + TL::LDS_B);
-      store_stage<CT>(An, An + TL::LDS_A, ra, rb);
-    }
+    u16 *cur = lds + (kt & 1) * TL::STAGE;
+    u16 *nxt = lds + ((kt & 1) ^ 1) * TL::STAGE;
+    gemm_step<CT>(cur, cur + TL::LDS_A, nxt, kt + 1 < nk, (kt + 1) * kBK, dma, xb, a.w, wave, wn, wm, l16, g4, acc);
+    wait_vmem_upto<0>();
     __syncthreads();
   }
 
@@ -158,7 +194,7 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16_kernel(GemmArgs a, uint32_t 
   const int nw0 = n0 + wn * TL::WN;   // first channel of this wave
   if constexpr (MODE == 0) {
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
+    for (int tt = 0; tt < kTT; ++tt) {
       const int64_t r = m0 + wm * kWM + tt * 16 + l16;
       if (r >= a.M) continue;
 #pragma unroll
@@ -178,7 +214,7 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16_kernel(GemmArgs a, uint32_t 
 
 // MODE 1 epilogue: the wave's channels are HPW whole heads.
 template <int CT, int D>
-__device__ __forceinline__ void epilogue_qkv(const GemmArgs &a, f32x4 (&acc)[CT][4], int64_t m0, int nw0, int wm,
+__device__ __forceinline__ void epilogue_qkv(const GemmArgs &a, f32x4 (&acc)[CT][kTT], int64_t m0, int nw0, int wm,
                                              int l16, int g4) {
   typedef Tile<CT> TL;
   constexpr int HPW = TL::WN / D;
@@ -189,7 +225,7 @@ __device__ __forceinline__ void epilogue_qkv(const GemmArgs &a, f32x4 (&acc)[CT]
   const int npairs = a.rope.kind == ST_ROPE_2D ? D / 4 : D / 2;
 
 #pragma unroll
-  for (int tt = 0; tt < 4; ++tt) {
+  for (int tt = 0; tt < kTT; ++tt) {
     const int64_t r = m0 + wm * kWM + tt * 16 + l16;
     // per-head sum of squares over this lane's channels, then over the 4 lanes of the token
     float ss[HPW];
@@ -276,7 +312,7 @@ st_status launch_gemm(const GemmArgs &a, hipStream_t s) {
   const uint32_t nt = (a.N + TL::BN - 1) / TL::BN;
   const int64_t nb = mt * nt;
   if (nb >= (1ll << 31)) return ST_EUNSUPPORTED;
-  hipLaunchKernelGGL((gemm_bf16_kernel<CT, MODE, D>), dim3((uint32_t)nb), dim3(256), 0, s, a, nt, (uint32_t)nb);
+  hipLaunchKernelGGL((gemm_bf16_kernel<CT, MODE, D>), dim3((uint32_t)nb), dim3(kThreads), 0, s, a, nt, (uint32_t)nb);
   return launch_status();
 }
 

@@ -160,7 +160,7 @@ st_status st_qkv_norm_rope(const void *x, int64_t rows, int c_in, const void *w_
   if (rope_kind != ST_ROPE_NONE && rope_kind != ST_ROPE_1D && rope_kind != ST_ROPE_2D) return ST_EINVAL;
   if (d < 2 || d % 2 || (rope_kind == ST_ROPE_2D && d % 4)) return ST_EINVAL;
   if (!head_dim_ok(d, dtype, rope_kind)) return ST_EUNSUPPORTED;
-  if (dtype == ST_BF16 && c_in % 8) return ST_EUNSUPPORTED;
+  if (dtype == ST_BF16 && c_in % 64) return ST_EUNSUPPORTED;
   const st_status rs = check_rope(rope_kind, rope_table, rope_npos, pos_period, pos_offset, grid_w, d, rows);
   if (rs != ST_OK) return rs;
   if ((int64_t)H * d * 3 >= (1 << 30) || rows >= (1ll << 40)) return ST_EUNSUPPORTED;
@@ -181,7 +181,7 @@ st_status st_out_proj(const void *a, int64_t rows, int k_in, const void *w, int 
                       void *stream) {
   if (!dtype_ok(dtype)) return ST_EINVAL;
   if (!a || !w || !y || rows < 0 || k_in < 1 || n_out < 1) return ST_EINVAL;
-  if (n_out % 4 || (dtype == ST_BF16 && k_in % 8)) return ST_EUNSUPPORTED;
+  if (n_out % 4 || (dtype == ST_BF16 && k_in % 64)) return ST_EUNSUPPORTED;
   if (rows >= (1ll << 40) || (int64_t)k_in * n_out >= (1ll << 40)) return ST_EUNSUPPORTED;
   if (!aligned16(a) || !aligned16(w) || !aligned16(y)) return ST_EALIGN;
   const size_t e = esize(dtype);
@@ -260,7 +260,7 @@ st_status st_block_sliced(const void *x, int B, int T, int t_valid, int S, int g
   if (d < 4 || d % 4) return ST_EINVAL;
   if (!(eps >= 0.f) || !isfinite(eps) || !(rope_base > 0.f) || !isfinite(rope_base)) return ST_EINVAL;
   if (!head_dim_ok(d, dtype, ST_ROPE_2D)) return ST_EUNSUPPORTED;
-  if (dtype == ST_BF16 && (C % 8 || (H * d) % 8)) return ST_EUNSUPPORTED;
+  if (dtype == ST_BF16 && (C % 64 || (H * d) % 64)) return ST_EUNSUPPORTED;
   if (C % 4) return ST_EUNSUPPORTED;
   if ((int64_t)B * T * S >= (1ll << 32) / 2) return ST_EUNSUPPORTED;
   for (const st_layer_weights *w : {spatial, temporal})

@@ -73,7 +73,9 @@ def qkv_args(**kw):
     (dict(d=70), st.ST_EINVAL),                       # 2D RoPE needs d % 4 == 0
     (dict(d=96), st.ST_EUNSUPPORTED),                 # no bf16 kernel for d = 96
     (dict(d=256, dtype=st.ST_F32), st.ST_EUNSUPPORTED),
-    (dict(c_in=1150), st.ST_EUNSUPPORTED),            # bf16 needs c_in % 8 == 0
+    (dict(c_in=1150), st.ST_EUNSUPPORTED),            # bf16 needs c_in % 64 == 0
+    (dict(c_in=1160), st.ST_EUNSUPPORTED),
+    (dict(c_in=1120), st.ST_EUNSUPPORTED),
     (dict(rope_kind=5), st.ST_EINVAL),
     (dict(rope_table=None), st.ST_EINVAL),
     (dict(rope_npos=60, rows=8160), st.ST_EINVAL),   # h up to 67 not in table
@@ -92,6 +94,7 @@ def test_qkv_validation(kw, want):
     ((None, 10, 1152, P2, 1152, st.ST_BF16, BIG), st.ST_EINVAL),
     ((P, 10, 1152, P2, 1150, st.ST_BF16, BIG), st.ST_EUNSUPPORTED),
     ((P, 10, 1151, P2, 1152, st.ST_BF16, BIG), st.ST_EUNSUPPORTED),
+    ((P, 10, 1160, P2, 1152, st.ST_BF16, BIG), st.ST_EUNSUPPORTED),
     ((P, 10, 1152, P2, 1152, 3, BIG), st.ST_EINVAL),
     ((P, 10, 1152, P2, 1152, st.ST_BF16, P + 16), st.ST_EINVAL),    # y overlaps a
     ((P, 10, 1152, P2, 1152, st.ST_BF16, BIG + 2), st.ST_EALIGN),
