@@ -130,6 +130,7 @@ struct LongCfg {
   static constexpr int SLACK = 32;                // u16 after a tile: operand reads run past the last row
   static constexpr int REGION = TILE + SLACK;
   static constexpr int STAGE = 2 * REGION;        // K tile, then V tile
+  static constexpr int NSTAGE = 3;                // tiles in LDS at once
   static constexpr int BLOCKS = TILE * 2 / 1024;  // 1 KB direct-to-LDS loads per tile
   static_assert((TILE * 2) % 1024 == 0, "tile must be whole 1 KB blocks");
 };
@@ -148,7 +149,11 @@ struct LongDma {
   typedef LongCfg<D, 1> C;
   static constexpr int PER_WAVE = (2 * C::BLOCKS + C::WAVES - 1) / C::WAVES;
   int off[PER_WAVE];   // element offset of this lane's chunk within a tile
-  int key[PER_WAVE];   // key of this lane's chunk within a tile
+
+  __device__ __forceinline__ static int chunk_key(int n, int lane) {
+    const int b = n >= C::BLOCKS ? n - C::BLOCKS : n;
+    return (b * 64 + lane) / Dims<D>::CH;
+  }
 
   __device__ __forceinline__ void init(int64_t rs, int lane, int wave) {
 #pragma unroll
@@ -156,13 +161,12 @@ struct LongDma {
       const int n = wave + C::WAVES * i;
       const int b = n >= C::BLOCKS ? n - C::BLOCKS : n;
       const int c = b * 64 + lane;
-      key[i] = c / Dims<D>::CH;
-      off[i] = (int)(key[i] * rs) + (c % Dims<D>::CH) * 8;
+      off[i] = (int)((c / Dims<D>::CH) * rs) + (c % Dims<D>::CH) * 8;
     }
   }
 
   __device__ __forceinline__ void issue(u16 *__restrict__ dst_stage, int kb, const u16 *kp, const u16 *vp, int64_t rs,
-                                        int L, int wave) const {
+                                        int L, int lane, int wave) const {
     const bool tail = kb + C::KB > L;
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
@@ -172,7 +176,10 @@ struct LongDma {
         const int b = isv ? n - C::BLOCKS : n;
         const u16 *base = (isv ? vp : kp) + (int64_t)kb * rs;
         int o = off[i];
-        if (tail && kb + key[i] >= L) o += (int)((L - 1 - kb - key[i]) * rs);   // repeat row L-1
+        if (tail) {   // repeat row L-1 for keys past L
+          const int key = chunk_key(n, lane);
+          if (kb + key >= L) o += (int)((L - 1 - kb - key) * rs);
+        }
         u16 *dst = dst_stage + (isv ? C::REGION : 0) + b * 512;
         __builtin_amdgcn_global_load_lds(base + o, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
       }
@@ -180,57 +187,108 @@ struct LongDma {
   }
 };
 
-// One 64-key tile for one wave: issue the next tile's loads into `nxt`, then
-// S^T = K Q^T, online softmax, O^T += V^T P^T on the tile in Ks / Vs.  The
-// three stage pointers are restrict-qualified: the next tile's loads never
-// alias the tile being read.
+// Per-wave state and steps of the long kernel.  The key loop runs in units of
+// 32 keys and is software-pipelined: one step issues S^T = K Q^T of unit u+1,
+// then the exponentials of unit u (whose rescale is already settled), then
+// O^T += V^T P^T of unit u, and only then the rescale test of unit u+1.  The
+// matrix products of one unit and the vector work of the other are
+// independent, so the MFMA pipe and the vector ALU stay busy together.
+//
+// d = 72 (FOLD): the Q.K contraction is padded to 80 dimensions, and two of
+// the spare ones carry the softmax bookkeeping into the MFMA.  Q is
+// pre-multiplied by scale * log2(e); Q dim 72 holds -m (the running max in
+// those units, kept bf16-exact) against K dim 72 = 1, and Q dim 73 holds -1
+// against K dim 73 = 0 for a valid key or 2^120 for a masked one.  The
+// accumulator then is already c*s - m (or about -2^120), so a probability is
+// one exp2 and masking costs nothing in the loop.
+constexpr uint32_t kBf16One = 0x3F80u, kBf16NegOne = 0xBF80u, kBf16Big = 0x7B80u;   // 1, -1, 2^120
+
+__device__ __forceinline__ float round_bf16(float x) { return __uint_as_float(pack_bf16x2(x, 0.f) << 16); }
+
 template <int D, int NT>
-__device__ __forceinline__ void long_tile(const u16 *__restrict__ Ks, const u16 *__restrict__ Vs,
-                                          u16 *__restrict__ nxt, bool prefetch, int kt, const AttnArgs &a,
-                                          const LongDma<D> &dma, const u16 *kp, const u16 *vp, int64_t rs, int L,
-                                          int nv, int lane, int g,
-                                          int l32, int wave, int v_off, bool vkeep, uint32_t vconst,
-                                          const bf16x8 (&qf)[NT][Dims<D>::KS], f32x16 (&oacc)[Dims<D>::DT][NT],
-                                          float (&mref)[NT], float (&lsum)[NT]) {
+struct LongWave {
   typedef LongCfg<D, NT> C;
   typedef Dims<D> DM;
-  if (prefetch) dma.issue(nxt, (kt + 1) * C::KB, kp, vp, rs, L, wave);
-  const int kb = kt * C::KB;
-  const bool masked = kb + C::KB > nv;
-#pragma unroll
-  for (int sub = 0; sub < 2; ++sub) {
-    f32x16 s[NT];
+  static constexpr bool FOLD = DM::DQK > D;
+  static_assert(!FOLD || D % 16 == 8, "the folded terms sit in the upper half of the last Q.K step");
+
+  bf16x8 qf[NT][DM::KS];     // Q^T operand (B of S^T = K Q^T)
+  f32x16 oacc[DM::DT][NT];   // O^T accumulator
+  float m[NT];               // running max: FOLD, scaled log2 units; else raw scores
+  float lsum[NT];            // softmax denominator when V^T has no ones row
+  float c;                   // scale * log2(e)
+  int nv, l32, g, v_off;
+  bool vkeep;                // lane's row of the last P.V tile is a real V^T row
+  uint32_t vconst;           // otherwise its constant (ones row or zero)
+
+  // S^T of the 32 keys of unit u, whose K rows start at Ks.
+  __device__ __forceinline__ void qk(f32x16 (&s)[NT], const u16 *__restrict__ Ks, int u) const {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[nt][r] = 0.f;
+    uint32_t kfix = 0;
+    if constexpr (FOLD) kfix = u * 32 + l32 < nv ? kBf16One : (kBf16One | kBf16Big << 16);
 #pragma unroll
     for (int ks = 0; ks < DM::KS; ++ks) {
-      const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(Ks + (sub * 32 + l32) * D + ks * 16 + g * 8);
+      uint4 ku = *reinterpret_cast<const uint4 *>(Ks + l32 * D + ks * 16 + g * 8);
+      if constexpr (FOLD)
+        if (ks == DM::KS - 1 && g) ku.x = kfix;
+      const bf16x8 kf = __builtin_bit_cast(bf16x8, ku);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) s[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[nt][ks], s[nt], 0, 0, 0);
     }
-    if (masked) {
+  }
+
+  // Keys of unit u at or past nv get score -inf (the FOLD path masks in qk).
+  __device__ __forceinline__ void mask(f32x16 (&s)[NT], int u) const {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const bool off = kb + sub * 32 + acc_row(r, g) >= nv;
+    for (int r = 0; r < 16; ++r) {
+      const bool off = u * 32 + acc_row(r, g) >= nv;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) s[nt][r] = off ? -INFINITY : s[nt][r];
-      }
+      for (int nt = 0; nt < NT; ++nt) s[nt][r] = off ? -INFINITY : s[nt][r];
     }
-    float mx[NT];
+  }
+
+  // Lane-local maxima of a unit's scores; true when some query's running
+  // max must move (its scores exceed it by more than 2^kRescale).
+  __device__ __forceinline__ bool needs_rescale(const f32x16 (&s)[NT], float (&lm)[NT]) const {
     bool grow = false;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      mx[nt] = max_across_halves(max16(s[nt]));
-      grow |= (mx[nt] - mref[nt]) * a.c > kRescale;
+      lm[nt] = max16(s[nt]);
+      if constexpr (FOLD) grow |= lm[nt] > kRescale;
+      else grow |= (lm[nt] - m[nt]) * c > kRescale;
     }
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+    return __builtin_amdgcn_ballot_w64(grow) != 0;
+  }
+
+  // Move the running max to cover unit s; `first`: nothing is accumulated yet.
+  __device__ __forceinline__ void rescale(f32x16 (&s)[NT], const float (&lm)[NT], bool first) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const float mnew = fmaxf(mref[nt], mx[nt]);
-        const float alpha = __builtin_amdgcn_exp2f((mref[nt] - mnew) * a.c);
-        mref[nt] = mnew;
+    for (int nt = 0; nt < NT; ++nt) {
+      const float mx = max_across_halves(lm[nt]);
+      if constexpr (FOLD) {
+        // s holds c*score - m; the new max is bf16-exact so -m fits Q dim 72.
+        const float mnew = round_bf16(m[nt] + (first ? mx : fmaxf(mx, 0.f)));
+        const float delta = mnew - m[nt];
+        if (!first) {
+          const float alpha = __builtin_amdgcn_exp2f(-delta);
+#pragma unroll
+          for (int dt = 0; dt < DM::DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[dt][nt][r] *= alpha;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[nt][r] -= delta;
+        m[nt] = mnew;
+        uint4 qu = __builtin_bit_cast(uint4, qf[nt][DM::KS - 1]);
+        if (g) qu.x = (kBf16NegOne << 16) | ((__float_as_uint(mnew) >> 16) ^ 0x8000u);
+        qf[nt][DM::KS - 1] = __builtin_bit_cast(bf16x8, qu);
+      } else {
+        const float mnew = fmaxf(m[nt], mx);
+        const float alpha = __builtin_amdgcn_exp2f((m[nt] - mnew) * c);   // 0 when first
+        m[nt] = mnew;
         lsum[nt] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DM::DT; ++dt)
@@ -238,49 +296,81 @@ __device__ __forceinline__ void long_tile(const u16 *__restrict__ Ks, const u16 
           for (int r = 0; r < 16; ++r) oacc[dt][nt][r] *= alpha;
       }
     }
+  }
+
+  // Probabilities of a settled unit, as the bf16 B operand of O^T = V^T P^T.
+  __device__ __forceinline__ void probs(f32x16 (&s)[NT], bf16x8 (&pf)[2][NT]) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const float mc = mref[nt] * a.c;
+      if constexpr (FOLD) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[nt][r] = __builtin_amdgcn_exp2f(fmaf(s[nt][r], a.c, -mc));
+        for (int r = 0; r < 16; ++r) s[nt][r] = __builtin_amdgcn_exp2f(s[nt][r]);
+      } else {
+        const float mc = m[nt] * c;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[nt][r] = __builtin_amdgcn_exp2f(fmaf(s[nt][r], c, -mc));
+      }
       if constexpr (!DM::ONES) {
         float acc = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc += s[nt][r];
         lsum[nt] += acc;
       }
+      pf[0][nt] = pack_p(s[nt], 0);
+      pf[1][nt] = pack_p(s[nt], 8);
     }
+  }
+
+  // O^T += V^T P^T for one unit whose V rows start at Vs.
+  __device__ __forceinline__ void pv(const bf16x8 (&pf)[2][NT], const u16 *__restrict__ Vs) {
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2) {
-      bf16x8 pf[NT];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) pf[nt] = pack_p(s[nt], ks2 * 8);
-      const u16 *vb = Vs + (sub * 32 + ks2 * 16) * D + v_off;
+      const u16 *vb = Vs + ks2 * 16 * D + v_off;
 #pragma unroll
       for (int dt = 0; dt < DM::DT; ++dt) {
         typedef short v4s __attribute__((ext_vector_type(4)));
-        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4s *)(vb + dt * 32));
-        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4s *)(vb + dt * 32 + 8 * D));
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(vb + dt * 32));
+        const v4s hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(vb + dt * 32 + 8 * D));
         uint4 u = make_uint4(__builtin_bit_cast(uint2, lo).x, __builtin_bit_cast(uint2, lo).y,
                              __builtin_bit_cast(uint2, hi).x, __builtin_bit_cast(uint2, hi).y);
         if (DM::DV != D && dt == DM::DT - 1 && !vkeep) u = make_uint4(vconst, vconst, vconst, vconst);
         const bf16x8 vf = __builtin_bit_cast(bf16x8, u);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
-          oacc[dt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[nt], oacc[dt][nt], 0, 0, 0);
+          oacc[dt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks2][nt], oacc[dt][nt], 0, 0, 0);
       }
     }
   }
-}
+
+  // One pipeline step: unit u (settled, scores in s, V rows at Vs) and, when
+  // NEXT, unit un (K rows at Kn), whose scores replace s on return.
+  template <bool NEXT>
+  __device__ __forceinline__ void step(f32x16 (&s)[NT], const u16 *__restrict__ Vs, const u16 *__restrict__ Kn,
+                                       int un, bool mask_next) {
+    f32x16 sn[NT];
+    if constexpr (NEXT) qk(sn, Kn, un);
+    bf16x8 pf[2][NT];
+    probs(s, pf);
+    pv(pf, Vs);
+    if constexpr (NEXT) {
+      if constexpr (!FOLD)
+        if (mask_next) mask(sn, un);
+      float lm[NT];
+      if (needs_rescale(sn, lm)) rescale(sn, lm, false);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) s[nt] = sn[nt];
+    }
+  }
+};
 
 template <int D, int NT>
 __global__ void __launch_bounds__(64 * kLongWaves, 8 / kLongWaves) attn_long_kernel(AttnArgs a, uint32_t nqb,
                                                                                   uint32_t nblocks) {
   typedef LongCfg<D, NT> C;
   typedef Dims<D> DM;
-  __shared__ __attribute__((aligned(16))) u16 lds[2 * C::STAGE];
+  typedef LongWave<D, NT> W;
+  __shared__ __attribute__((aligned(16))) u16 lds[C::NSTAGE * C::STAGE];
 
   const uint32_t tile = xcd_remap(blockIdx.x, nblocks);
   const uint32_t qb = tile % nqb;
@@ -294,40 +384,51 @@ __global__ void __launch_bounds__(64 * kLongWaves, 8 / kLongWaves) attn_long_ker
 
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
-  const int l32 = lane & 31, g = lane >> 5;
-  const int L = a.L, nv = a.n_valid;
+  const int L = a.L;
+
+  W w;
+  w.c = a.c;
+  w.nv = min(L, a.n_valid);
+  w.l32 = lane & 31;
+  w.g = lane >> 5;
 
   // Slack after every tile is zero, so operand reads that run past the last
   // row multiply finite values by the zero padding of Q (K) or get replaced (V).
-  for (int i = t; i < 4 * C::SLACK; i += 64 * C::WAVES) lds[(i / C::SLACK) * C::REGION + C::TILE + i % C::SLACK] = 0;
+  for (int i = t; i < 2 * C::NSTAGE * C::SLACK; i += 64 * C::WAVES)
+    lds[(i / C::SLACK) * C::REGION + C::TILE + i % C::SLACK] = 0;
 
-  // Q operand fragments (B of S^T = K Q^T), held for the whole key loop.
+  // Q operand fragments, held for the whole key loop (FOLD: times c, plus
+  // the -m and -1 terms; m starts at 0).
   const int q0 = qb * C::QB + wave * C::QW;
-  bf16x8 qf[NT][DM::KS];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const int qi = q0 + nt * 32 + l32;
+    const int qi = q0 + nt * 32 + w.l32;
 #pragma unroll
     for (int ks = 0; ks < DM::KS; ++ks) {
-      const int dd = ks * 16 + g * 8;
+      const int dd = ks * 16 + w.g * 8;
       uint4 u = make_uint4(0, 0, 0, 0);
       if (qi < L && dd < D) u = *reinterpret_cast<const uint4 *>(qp + (int64_t)qi * rs + dd);
-      qf[nt][ks] = __builtin_bit_cast(bf16x8, u);
+      if constexpr (W::FOLD) {
+        uint32_t x[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          x[j] = pack_bf16x2(__uint_as_float(x[j] << 16) * w.c, __uint_as_float(x[j] & 0xFFFF0000u) * w.c);
+        u = make_uint4(x[0], x[1], x[2], x[3]);
+        if (ks == DM::KS - 1 && w.g) u.x = kBf16NegOne << 16;
+      }
+      w.qf[nt][ks] = __builtin_bit_cast(bf16x8, u);
     }
   }
-
-  f32x16 oacc[DM::DT][NT];
 #pragma unroll
   for (int i = 0; i < DM::DT; ++i)
 #pragma unroll
     for (int j = 0; j < NT; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[i][j][r] = 0.f;
-  float mref[NT], lsum[NT];
+      for (int r = 0; r < 16; ++r) w.oacc[i][j][r] = 0.f;
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
-    mref[j] = -INFINITY;
-    lsum[j] = 0.f;
+    w.m[j] = W::FOLD ? 0.f : -INFINITY;
+    w.lsum[j] = 0.f;
   }
 
   // V^T operand via LDS transpose reads (ds_read_b64_tr_b16): in each 16-lane
@@ -336,27 +437,59 @@ __global__ void __launch_bounds__(64 * kLongWaves, 8 / kLongWaves) attn_long_ker
   // with dg = 32 dt + 16 (G & 1), so lane i of the group gets 4 consecutive keys
   // of dimension dg + i: exactly the A-operand layout (row = lane % 32).
   const int grp = lane >> 4, gi = lane & 15;
-  const int v_off = (gi >> 2) * D + 16 * (grp & 1) + 4 * (gi & 3) + 4 * (grp >> 1) * D;
+  w.v_off = (gi >> 2) * D + 16 * (grp & 1) + 4 * (gi & 3) + 4 * (grp >> 1) * D;
   // rows past D in the last P.V tile: the ones row, then zeros
-  const int dlast = 32 * (DM::DT - 1) + l32;
-  const bool vkeep = dlast < D;
-  const uint32_t vconst = (DM::ONES && dlast == D) ? 0x3F803F80u : 0u;
+  const int dlast = 32 * (DM::DT - 1) + w.l32;
+  w.vkeep = dlast < D;
+  w.vconst = (DM::ONES && dlast == D) ? 0x3F803F80u : 0u;
 
-  const int nkt = (min(L, nv) + C::KB - 1) / C::KB;   // tiles past n_valid carry no weight
+  // Units of 32 keys up to n_valid (later keys carry no weight), two per
+  // 64-key LDS tile.  Tiles rotate through NSTAGE stages: tile j+1 is in
+  // flight while tile j is read, and the step that finishes tile j-1's V
+  // reads runs after the barrier that opens tile j.
+  const int nu = (w.nv + 31) / 32;
+  const int ntl = (nu + 1) / 2;
+  const bool partial = (w.nv & 31) != 0;
   LongDma<D> dma;
   dma.init(rs, lane, wave);
-  if (nkt > 0) dma.issue(lds, 0, kp, vp, rs, L, wave);
+  if (ntl == 0) return;   // whole workgroup: n_valid is uniform
+  dma.issue(lds, 0, kp, vp, rs, L, lane, wave);
   wait_vmem();
   __syncthreads();
+  if (ntl > 1) dma.issue(lds + C::STAGE, C::KB, kp, vp, rs, L, lane, wave);
 
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int stage = kt & 1;
-    u16 *cur = lds + stage * C::STAGE;
-    u16 *nxt = lds + (stage ^ 1) * C::STAGE;
-    long_tile<D, NT>(cur, cur + C::REGION, nxt, kt + 1 < nkt, kt, a, dma, kp, vp, rs, L, nv, lane, g, l32, wave, v_off,
-                     vkeep, vconst, qf, oacc, mref, lsum);
+  f32x16 s[NT];
+  {
+    w.qk(s, lds, 0);
+    if constexpr (!W::FOLD)
+      if (partial && nu == 1) w.mask(s, 0);
+    float lm[NT];
+    w.needs_rescale(s, lm);
+    w.rescale(s, lm, true);
+  }
+
+  int st = 0;   // stage of tile kt
+  for (int kt = 0; kt + 1 < ntl; ++kt) {
+    const u16 *Ks = lds + st * C::STAGE;
+    const u16 *Vs = Ks + C::REGION;
+    const int st1 = st == C::NSTAGE - 1 ? 0 : st + 1;
+    const int st2 = st1 == C::NSTAGE - 1 ? 0 : st1 + 1;
+    w.template step<true>(s, Vs, Ks + 32 * D, 2 * kt + 1, partial && 2 * kt + 1 == nu - 1);
     wait_vmem();
     __syncthreads();
+    if (kt + 2 < ntl) dma.issue(lds + st2 * C::STAGE, (kt + 2) * C::KB, kp, vp, rs, L, lane, wave);
+    w.template step<true>(s, Vs + 32 * D, lds + st1 * C::STAGE, 2 * kt + 2, partial && 2 * kt + 2 == nu - 1);
+    st = st1;
+  }
+  {
+    const u16 *Ks = lds + st * C::STAGE;
+    const u16 *Vs = Ks + C::REGION;
+    if (2 * ntl == nu) {
+      w.template step<true>(s, Vs, Ks + 32 * D, nu - 1, partial);
+      w.template step<false>(s, Vs + 32 * D, nullptr, 0, false);
+    } else {
+      w.template step<false>(s, Vs, nullptr, 0, false);
+    }
   }
 
   // normalise and store
@@ -364,24 +497,24 @@ __global__ void __launch_bounds__(64 * kLongWaves, 8 / kLongWaves) attn_long_ker
   for (int nt = 0; nt < NT; ++nt) {
     float l;
     if constexpr (DM::ONES) {
-      l = __shfl(oacc[DM::ONES_DT][nt][DM::ONES_R], l32);   // held by lane half 0
+      l = __shfl(w.oacc[DM::ONES_DT][nt][DM::ONES_R], w.l32);   // held by lane half 0
     } else {
-      l = lsum[nt] + __shfl_xor(lsum[nt], 32);
+      l = w.lsum[nt] + __shfl_xor(w.lsum[nt], 32);
     }
     const float inv = 1.0f / l;
-    const int qi = q0 + nt * 32 + l32;
+    const int qi = q0 + nt * 32 + w.l32;
     if (qi >= L) continue;
     u16 *orow = op + (int64_t)qi * rs;
 #pragma unroll
     for (int dt = 0; dt < DM::DT; ++dt)
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
-        const int dd = dt * 32 + rb * 8 + g * 4;
+        const int dd = dt * 32 + rb * 8 + w.g * 4;
         if (dd + 4 <= D) {
-          uint2 w;
-          w.x = pack_bf16x2(oacc[dt][nt][rb * 4 + 0] * inv, oacc[dt][nt][rb * 4 + 1] * inv);
-          w.y = pack_bf16x2(oacc[dt][nt][rb * 4 + 2] * inv, oacc[dt][nt][rb * 4 + 3] * inv);
-          *reinterpret_cast<uint2 *>(orow + dd) = w;
+          uint2 o;
+          o.x = pack_bf16x2(w.oacc[dt][nt][rb * 4 + 0] * inv, w.oacc[dt][nt][rb * 4 + 1] * inv);
+          o.y = pack_bf16x2(w.oacc[dt][nt][rb * 4 + 2] * inv, w.oacc[dt][nt][rb * 4 + 3] * inv);
+          *reinterpret_cast<uint2 *>(orow + dd) = o;
         }
       }
   }
