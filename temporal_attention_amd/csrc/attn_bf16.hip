@@ -55,7 +55,21 @@ struct Dims {
   // location of the ones row inside O^T: tile, register, lane half
   static constexpr int ONES_DT = D / 32;
   static constexpr int ONES_R = ((D % 32) / 8) * 4 + (D % 4);
+  // Long kernel: when the rows past the last whole 32-row tile (the tail of
+  // d, the ones row) fit in 16, they form one 16-row tile on the 16x16x32 MFMA.
+  static constexpr bool PV16 = ONES && (D % 32) < 16;
+  static constexpr int DT32 = PV16 ? D / 32 : DT;   // 32-row P.V tiles
 };
+
+// Two LDS transpose reads, 8 keys apart, as one 8 x bf16 MFMA operand.
+template <int D>
+__device__ __forceinline__ uint4 tr_read_pair(const u16 *p) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)p);
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(p + 8 * D));
+  const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
+  return make_uint4(a.x, a.y, b.x, b.y);
+}
 
 __device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
 __device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
@@ -213,20 +227,17 @@ struct LongWave {
   static_assert(!FOLD || D % 16 == 8, "the folded terms sit in the upper half of the last Q.K step");
 
   bf16x8 qf[NT][DM::KS];     // Q^T operand (B of S^T = K Q^T)
-  f32x16 oacc[DM::DT][NT];   // O^T accumulator
+  f32x16 oacc[DM::DT32][NT]; // O^T accumulator, 32-row tiles
+  f32x4 oacc16[NT][2];       // PV16: last 16 rows of O^T, queries 0..15 and 16..31 of a tile
   float m[NT];               // running max: FOLD, scaled log2 units; else raw scores
   float lsum[NT];            // softmax denominator when V^T has no ones row
   float c;                   // scale * log2(e)
-  int nv, l32, g, v_off;
+  int nv, l32, g, q16, v_off, v_off16;
   bool vkeep;                // lane's row of the last P.V tile is a real V^T row
   uint32_t vconst;           // otherwise its constant (ones row or zero)
 
-  // S^T of the 32 keys of unit u, whose K rows start at Ks.
-  __device__ __forceinline__ void qk(f32x16 (&s)[NT], const u16 *__restrict__ Ks, int u) const {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[nt][r] = 0.f;
+  // K operand of the 32 keys of unit u, whose K rows start at Ks.
+  __device__ __forceinline__ void kfrag(bf16x8 (&kf)[DM::KS], const u16 *__restrict__ Ks, int u) const {
     uint32_t kfix = 0;
     if constexpr (FOLD) kfix = u * 32 + l32 < nv ? kBf16One : (kBf16One | kBf16Big << 16);
 #pragma unroll
@@ -234,10 +245,23 @@ struct LongWave {
       uint4 ku = *reinterpret_cast<const uint4 *>(Ks + l32 * D + ks * 16 + g * 8);
       if constexpr (FOLD)
         if (ks == DM::KS - 1 && g) ku.x = kfix;
-      const bf16x8 kf = __builtin_bit_cast(bf16x8, ku);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) s[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[nt][ks], s[nt], 0, 0, 0);
+      kf[ks] = __builtin_bit_cast(bf16x8, ku);
     }
+  }
+
+  // S^T of one 32-query tile.
+  __device__ __forceinline__ void qk(f32x16 &s, const bf16x8 (&kf)[DM::KS], int nt) const {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < DM::KS; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[nt][ks], s, 0, 0, 0);
+  }
+
+  __device__ __forceinline__ void qk(f32x16 (&s)[NT], const u16 *__restrict__ Ks, int u) const {
+    bf16x8 kf[DM::KS];
+    kfrag(kf, Ks, u);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) qk(s[nt], kf, nt);
   }
 
   // Keys of unit u at or past nv get score -inf (the FOLD path masks in qk).
@@ -272,13 +296,7 @@ struct LongWave {
         // s holds c*score - m; the new max is bf16-exact so -m fits Q dim 72.
         const float mnew = round_bf16(m[nt] + (first ? mx : fmaxf(mx, 0.f)));
         const float delta = mnew - m[nt];
-        if (!first) {
-          const float alpha = __builtin_amdgcn_exp2f(-delta);
-#pragma unroll
-          for (int dt = 0; dt < DM::DT; ++dt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[dt][nt][r] *= alpha;
-        }
+        if (!first) scale_acc(nt, __builtin_amdgcn_exp2f(-delta));
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[nt][r] -= delta;
         m[nt] = mnew;
@@ -290,35 +308,43 @@ struct LongWave {
         const float alpha = __builtin_amdgcn_exp2f((m[nt] - mnew) * c);   // 0 when first
         m[nt] = mnew;
         lsum[nt] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DM::DT; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[dt][nt][r] *= alpha;
+        scale_acc(nt, alpha);
       }
     }
   }
 
-  // Probabilities of a settled unit, as the bf16 B operand of O^T = V^T P^T.
-  __device__ __forceinline__ void probs(f32x16 (&s)[NT], bf16x8 (&pf)[2][NT]) {
+  // Whole-vector multiplies: element-wise ones make the register allocator
+  // copy the MFMA accumulators on every path through the rescale branch.
+  __device__ __forceinline__ void scale_acc(int nt, float alpha) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      if constexpr (FOLD) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[nt][r] = __builtin_amdgcn_exp2f(s[nt][r]);
-      } else {
-        const float mc = m[nt] * c;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[nt][r] = __builtin_amdgcn_exp2f(fmaf(s[nt][r], c, -mc));
-      }
-      if constexpr (!DM::ONES) {
-        float acc = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc += s[nt][r];
-        lsum[nt] += acc;
-      }
-      pf[0][nt] = pack_p(s[nt], 0);
-      pf[1][nt] = pack_p(s[nt], 8);
+    for (int dt = 0; dt < DM::DT32; ++dt) oacc[dt][nt] = oacc[dt][nt] * alpha;
+    if constexpr (DM::PV16) {
+      // the 16x16 accumulator holds query (lane & 15) + 16 h in every lane;
+      // alpha is per query in lane (query) of the 32x32 layout
+      oacc16[nt][0] = oacc16[nt][0] * __shfl(alpha, q16);
+      oacc16[nt][1] = oacc16[nt][1] * __shfl(alpha, q16 + 16);
     }
+  }
+
+  // Probabilities of query tile nt of a settled unit, as the bf16 B operand
+  // of O^T = V^T P^T.
+  __device__ __forceinline__ void probs(f32x16 &s, bf16x8 (&pf)[2][NT], int nt) {
+    if constexpr (FOLD) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(s[r]);
+    } else {
+      const float mc = m[nt] * c;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c, -mc));
+    }
+    if constexpr (!DM::ONES) {
+      float acc = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc += s[r];
+      lsum[nt] += acc;
+    }
+    pf[0][nt] = pack_p(s, 0);
+    pf[1][nt] = pack_p(s, 8);
   }
 
   // O^T += V^T P^T for one unit whose V rows start at Vs.
@@ -327,39 +353,63 @@ struct LongWave {
     for (int ks2 = 0; ks2 < 2; ++ks2) {
       const u16 *vb = Vs + ks2 * 16 * D + v_off;
 #pragma unroll
-      for (int dt = 0; dt < DM::DT; ++dt) {
-        typedef short v4s __attribute__((ext_vector_type(4)));
-        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(vb + dt * 32));
-        const v4s hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(vb + dt * 32 + 8 * D));
-        uint4 u = make_uint4(__builtin_bit_cast(uint2, lo).x, __builtin_bit_cast(uint2, lo).y,
-                             __builtin_bit_cast(uint2, hi).x, __builtin_bit_cast(uint2, hi).y);
-        if (DM::DV != D && dt == DM::DT - 1 && !vkeep) u = make_uint4(vconst, vconst, vconst, vconst);
+      for (int dt = 0; dt < DM::DT32; ++dt) {
+        uint4 u = tr_read_pair<D>(vb + dt * 32);
+        if (!DM::PV16 && DM::DV != D && dt == DM::DT - 1 && !vkeep) u = make_uint4(vconst, vconst, vconst, vconst);
         const bf16x8 vf = __builtin_bit_cast(bf16x8, u);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
           oacc[dt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks2][nt], oacc[dt][nt], 0, 0, 0);
       }
     }
+    if constexpr (DM::PV16) {
+      // The 16x16x32 B operand wants, per 16-lane row, 8 keys of 16 queries.
+      // v_permlane16_swap of the two 16-key halves of P^T regroups the score
+      // layout into exactly that: queries 0..15 (first result) and 16..31
+      // (second) of the tile, key groups {0-3,8-11}, {16-19,24-27},
+      // {4-7,12-15}, {20-23,28-31} by row; V^T is read in the same order.
+      uint4 u = tr_read_pair<D>(Vs + v_off16);
+      if (!vkeep) u = make_uint4(vconst, vconst, vconst, vconst);
+      const bf16x8 vf = __builtin_bit_cast(bf16x8, u);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const uint4 x0 = __builtin_bit_cast(uint4, pf[0][nt]), x1 = __builtin_bit_cast(uint4, pf[1][nt]);
+        const auto w0 = __builtin_amdgcn_permlane16_swap(x0.x, x1.x, false, false);
+        const auto w1 = __builtin_amdgcn_permlane16_swap(x0.y, x1.y, false, false);
+        const auto w2 = __builtin_amdgcn_permlane16_swap(x0.z, x1.z, false, false);
+        const auto w3 = __builtin_amdgcn_permlane16_swap(x0.w, x1.w, false, false);
+        const bf16x8 pa = __builtin_bit_cast(bf16x8, make_uint4(w0[0], w1[0], w2[0], w3[0]));
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(w0[1], w1[1], w2[1], w3[1]));
+        oacc16[nt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pa, oacc16[nt][0], 0, 0, 0);
+        oacc16[nt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb, oacc16[nt][1], 0, 0, 0);
+      }
+    }
   }
 
-  // One pipeline step: unit u (settled, scores in s, V rows at Vs) and, when
-  // NEXT, unit un (K rows at Kn), whose scores replace s on return.
-  template <bool NEXT>
-  __device__ __forceinline__ void step(f32x16 (&s)[NT], const u16 *__restrict__ Vs, const u16 *__restrict__ Kn,
-                                       int un, bool mask_next) {
-    f32x16 sn[NT];
-    if constexpr (NEXT) qk(sn, Kn, un);
+  // One pipeline step: unit u (settled, scores in slot CUR of sb, V rows at
+  // Vs) and, when NEXT, unit un (K rows at Kn), whose scores go to the other
+  // slot.  Steps alternate slots, so no scores are ever copied.  Phase nt
+  // pairs the S^T MFMAs of query tile nt of unit un with the exponentials of
+  // the same tile of unit u, so only one tile of each is in flight at once;
+  // the last phase pairs O^T += V^T P^T with the rescale test.
+  template <bool NEXT, int CUR>
+  __device__ __forceinline__ void step(f32x16 (&sb)[2][NT], const u16 *__restrict__ Vs,
+                                       const u16 *__restrict__ Kn, int un, bool mask_next) {
     bf16x8 pf[2][NT];
-    probs(s, pf);
+    bf16x8 kf[DM::KS];
+    if constexpr (NEXT) kfrag(kf, Kn, un);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      if constexpr (NEXT) qk(sb[CUR ^ 1][nt], kf, nt);
+      probs(sb[CUR][nt], pf, nt);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     pv(pf, Vs);
     if constexpr (NEXT) {
       if constexpr (!FOLD)
-        if (mask_next) mask(sn, un);
+        if (mask_next) mask(sb[CUR ^ 1], un);
       float lm[NT];
-      if (needs_rescale(sn, lm)) rescale(sn, lm, false);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) s[nt] = sn[nt];
+      if (needs_rescale(sb[CUR ^ 1], lm)) rescale(sb[CUR ^ 1], lm, false);
     }
   }
 };
@@ -391,6 +441,7 @@ __global__ void __launch_bounds__(64 * kLongWaves, 8 / kLongWaves) attn_long_ker
   w.nv = min(L, a.n_valid);
   w.l32 = lane & 31;
   w.g = lane >> 5;
+  w.q16 = lane & 15;
 
   // Slack after every tile is zero, so operand reads that run past the last
   // row multiply finite values by the zero padding of Q (K) or get replaced (V).
@@ -420,13 +471,17 @@ __global__ void __launch_bounds__(64 * kLongWaves, 8 / kLongWaves) attn_long_ker
     }
   }
 #pragma unroll
-  for (int i = 0; i < DM::DT; ++i)
+  for (int i = 0; i < DM::DT32; ++i)
 #pragma unroll
     for (int j = 0; j < NT; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) w.oacc[i][j][r] = 0.f;
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) w.oacc16[j][h][r] = 0.f;
     w.m[j] = W::FOLD ? 0.f : -INFINITY;
     w.lsum[j] = 0.f;
   }
@@ -442,6 +497,14 @@ __global__ void __launch_bounds__(64 * kLongWaves, 8 / kLongWaves) attn_long_ker
   const int dlast = 32 * (DM::DT - 1) + w.l32;
   w.vkeep = dlast < D;
   w.vconst = (DM::ONES && dlast == D) ? 0x3F803F80u : 0u;
+  if constexpr (DM::PV16) {
+    // 16-row tile: group G of 16 lanes holds keys {0,16,4,20}[G] + {0..3, 8..11};
+    // lane 4j + q of the group addresses V[key0 + j][d16 + 4q], d16 = first row of the tile.
+    constexpr int d16 = D - D % 32;
+    w.v_off16 = ((grp & 1) * 16 + (grp >> 1) * 4 + (gi >> 2)) * D + d16 + 4 * (gi & 3);
+    w.vkeep = gi < D % 32;
+    w.vconst = (gi == D % 32) ? 0x3F803F80u : 0u;
+  }
 
   // Units of 32 keys up to n_valid (later keys carry no weight), two per
   // 64-key LDS tile.  Tiles rotate through NSTAGE stages: tile j+1 is in
@@ -458,14 +521,14 @@ __global__ void __launch_bounds__(64 * kLongWaves, 8 / kLongWaves) attn_long_ker
   __syncthreads();
   if (ntl > 1) dma.issue(lds + C::STAGE, C::KB, kp, vp, rs, L, lane, wave);
 
-  f32x16 s[NT];
+  f32x16 sb[2][NT];
   {
-    w.qk(s, lds, 0);
+    w.qk(sb[0], lds, 0);
     if constexpr (!W::FOLD)
-      if (partial && nu == 1) w.mask(s, 0);
+      if (partial && nu == 1) w.mask(sb[0], 0);
     float lm[NT];
-    w.needs_rescale(s, lm);
-    w.rescale(s, lm, true);
+    w.needs_rescale(sb[0], lm);
+    w.rescale(sb[0], lm, true);
   }
 
   int st = 0;   // stage of tile kt
@@ -474,21 +537,21 @@ __global__ void __launch_bounds__(64 * kLongWaves, 8 / kLongWaves) attn_long_ker
     const u16 *Vs = Ks + C::REGION;
     const int st1 = st == C::NSTAGE - 1 ? 0 : st + 1;
     const int st2 = st1 == C::NSTAGE - 1 ? 0 : st1 + 1;
-    w.template step<true>(s, Vs, Ks + 32 * D, 2 * kt + 1, partial && 2 * kt + 1 == nu - 1);
+    w.template step<true, 0>(sb, Vs, Ks + 32 * D, 2 * kt + 1, partial && 2 * kt + 1 == nu - 1);
     wait_vmem();
     __syncthreads();
     if (kt + 2 < ntl) dma.issue(lds + st2 * C::STAGE, (kt + 2) * C::KB, kp, vp, rs, L, lane, wave);
-    w.template step<true>(s, Vs + 32 * D, lds + st1 * C::STAGE, 2 * kt + 2, partial && 2 * kt + 2 == nu - 1);
+    w.template step<true, 1>(sb, Vs + 32 * D, lds + st1 * C::STAGE, 2 * kt + 2, partial && 2 * kt + 2 == nu - 1);
     st = st1;
   }
   {
     const u16 *Ks = lds + st * C::STAGE;
     const u16 *Vs = Ks + C::REGION;
     if (2 * ntl == nu) {
-      w.template step<true>(s, Vs, Ks + 32 * D, nu - 1, partial);
-      w.template step<false>(s, Vs + 32 * D, nullptr, 0, false);
+      w.template step<true, 0>(sb, Vs, Ks + 32 * D, nu - 1, partial);
+      w.template step<false, 1>(sb, Vs + 32 * D, nullptr, 0, false);
     } else {
-      w.template step<false>(s, Vs, nullptr, 0, false);
+      w.template step<false, 0>(sb, Vs, nullptr, 0, false);
     }
   }
 
@@ -496,27 +559,51 @@ __global__ void __launch_bounds__(64 * kLongWaves, 8 / kLongWaves) attn_long_ker
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     float l;
-    if constexpr (DM::ONES) {
+    float lh[2] = {0.f, 0.f};   // PV16: denominators of the two query halves (ones row = row D % 32)
+    if constexpr (DM::PV16) {
+      static_assert(DM::PV16 == false || (D % 32) % 4 == 0, "ones row starts a 4-row lane group");
+      lh[0] = __shfl(w.oacc16[nt][0][0], 16 * ((D % 32) / 4) + (lane & 15));
+      lh[1] = __shfl(w.oacc16[nt][1][0], 16 * ((D % 32) / 4) + (lane & 15));
+      l = w.l32 < 16 ? lh[0] : lh[1];
+    } else if constexpr (DM::ONES) {
       l = __shfl(w.oacc[DM::ONES_DT][nt][DM::ONES_R], w.l32);   // held by lane half 0
     } else {
       l = w.lsum[nt] + __shfl_xor(w.lsum[nt], 32);
     }
     const float inv = 1.0f / l;
     const int qi = q0 + nt * 32 + w.l32;
-    if (qi >= L) continue;
-    u16 *orow = op + (int64_t)qi * rs;
+    if (qi < L) {
+      u16 *orow = op + (int64_t)qi * rs;
 #pragma unroll
-    for (int dt = 0; dt < DM::DT; ++dt)
+      for (int dt = 0; dt < DM::DT32; ++dt)
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        const int dd = dt * 32 + rb * 8 + w.g * 4;
-        if (dd + 4 <= D) {
-          uint2 o;
-          o.x = pack_bf16x2(w.oacc[dt][nt][rb * 4 + 0] * inv, w.oacc[dt][nt][rb * 4 + 1] * inv);
-          o.y = pack_bf16x2(w.oacc[dt][nt][rb * 4 + 2] * inv, w.oacc[dt][nt][rb * 4 + 3] * inv);
-          *reinterpret_cast<uint2 *>(orow + dd) = o;
+        for (int rb = 0; rb < 4; ++rb) {
+          const int dd = dt * 32 + rb * 8 + w.g * 4;
+          if (dd + 4 <= D) {
+            uint2 o;
+            o.x = pack_bf16x2(w.oacc[dt][nt][rb * 4 + 0] * inv, w.oacc[dt][nt][rb * 4 + 1] * inv);
+            o.y = pack_bf16x2(w.oacc[dt][nt][rb * 4 + 2] * inv, w.oacc[dt][nt][rb * 4 + 3] * inv);
+            *reinterpret_cast<uint2 *>(orow + dd) = o;
+          }
+        }
+    }
+    if constexpr (DM::PV16) {
+      // 16x16 accumulator: lane l holds rows 4 (l / 16) .. +3 for query (l & 15) of each half
+      const int dd = D - D % 32 + 4 * (lane >> 4);
+      if (dd + 4 <= D) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int qh = q0 + nt * 32 + h * 16 + (lane & 15);
+          if (qh < L) {
+            const float ih = 1.0f / lh[h];
+            uint2 o;
+            o.x = pack_bf16x2(w.oacc16[nt][h][0] * ih, w.oacc16[nt][h][1] * ih);
+            o.y = pack_bf16x2(w.oacc16[nt][h][2] * ih, w.oacc16[nt][h][3] * ih);
+            *reinterpret_cast<uint2 *>(op + (int64_t)qh * rs + dd) = o;
+          }
         }
       }
+    }
   }
 }
 
