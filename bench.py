@@ -10,14 +10,17 @@ projection with 1D RoPE, temporal attention, output projection, relayout
 back.  Inputs are seeded synthetic tensors already resident in HBM.
 
 The JSON line reports the whole-step throughput in algorithmic TFLOP/s, each
-kernel's average duration from HIP events recorded on the launch stream, a
-roofline entry for the dominant kernel (spatial attention), the slicing
-schedule's time (N_T = N_S = 4, T padded to 52), and the fp64 oracle timed
-on a bounded sample on the host cores.
+kernel's average duration from HIP events recorded on the launch stream, the
+relayout rate next to a same-run device-to-device copy of the same bytes, a
+roofline entry for the dominant kernel (spatial attention; its HBM traffic
+comes from the committed rocprofv3 counter summary when that summary matches
+the kernel source), the slicing schedule's time (N_T = N_S = 4, T padded to
+52), and the fp64 oracle timed on a bounded sample on the host cores.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -31,6 +34,31 @@ PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
 WORKLOADS = {"1080p": 3, "720p": 2}
+HERE = os.path.dirname(os.path.abspath(__file__))
+ATTN_SOURCE = os.path.join(HERE, "temporal_attention_amd", "csrc", "attn_bf16.hip")
+ATTN_TRAFFIC = os.path.join(HERE, "profiles", "attn_spatial_1080p_traffic.txt")
+
+
+def measured_traffic(path=ATTN_TRAFFIC, source=ATTN_SOURCE):
+    """HBM bytes per launch of the spatial attention kernel, from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, scaled by its copy-kernel
+    calibration factors; None if the summary is missing or was taken on a
+    different version of the kernel source."""
+    try:
+        kv = {}
+        with open(path) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        with open(source, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+        if kv.get("source_sha256") != sha:
+            return None
+        return 1024.0 * (float(kv["fetch_kib_per_dispatch"]) * float(kv["fetch_factor"])
+                         + float(kv["write_kib_per_dispatch"]) * float(kv["write_factor"]))
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def flops_and_bytes(B, T, S, C, H, d):
@@ -166,6 +194,20 @@ def main():
     relayout_gbs = (by["relayout_fwd"] + by["relayout_bwd"]) / relayout_ms / 1e6
     attn_achieved = fl["attn_spatial"] / per["attn_spatial"] / 1e9
 
+    # practical ceiling of a relayout: a plain device-to-device copy of the same bytes, same run
+    cp_dst = torch.empty_like(x)
+    for _ in range(3):
+        cp_dst.copy_(x)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(args.steps):
+        cp_dst.copy_(x)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = by["relayout_fwd"] / (c0.elapsed_time(c1) / args.steps) / 1e6
+    del cp_dst
+    traffic = measured_traffic()
+
     out = {
         "metric": METRIC,
         "value": round(total_flops / ms_per_step / 1e9, 2),
@@ -186,10 +228,15 @@ def main():
         "block_tflops_excl_relayout": round(total_flops / (ms_per_step - relayout_ms) / 1e9, 2),
         "relayout_gbs": round(relayout_gbs, 1),
         "relayout_frac_hbm_peak": round(relayout_gbs / PEAK_HBM_GBS, 4),
+        "device_copy_gbs": round(copy_gbs, 1),
+        "relayout_frac_of_device_copy": round(relayout_gbs / copy_gbs, 4),
         "kernels": kernels,
         "roofline": {"kernel": "attn_long_kernel<72,2> (spatial attention)", "bound": "mfma",
                      "achieved": round(attn_achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(attn_achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(attn_achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None if traffic is None else round(traffic / 1e9, 4),
+                     "traffic_unit": "GB of HBM traffic per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)",
+                     "algorithmic_bytes": round(4.0 * B * T * S * H * d * 2 / 1e9, 4)},
     }
 
     if not args.no_sliced:

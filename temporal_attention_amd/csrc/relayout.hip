@@ -7,8 +7,8 @@
 // destination and drops size-1 dimensions.  When the innermost dimension is
 // contiguous on both sides the copy moves whole rows (for the [B,T,S,C] <->
 // [B,S,T,C] permutation a row is one C-vector, 2304 bytes in bf16) with the
-// widest vector width that every row start allows, one wavefront per row so
-// the row's offsets are computed once and the lanes stream the row.  Short
+// widest vector width that every row start allows, one wavefront per pair of
+// rows so the rows' offsets are computed once and the lanes stream the rows.  Short
 // rows use a lane-per-vector kernel; a non-contiguous innermost dimension
 // falls back to a lane-per-element kernel.  Divisions by the dimension sizes
 // use precomputed multiply-shift constants (division by invariant integers).
@@ -77,30 +77,41 @@ template <> struct Vec<4> { typedef uint32_t T; };
 template <> struct Vec<2> { typedef uint16_t T; };
 template <> struct Vec<1> { typedef uint8_t T; };
 
-// One wavefront per row; lanes stride the row in VB-byte vectors.
+// One wavefront per kRows rows; lanes stride each row in VB-byte vectors.  A
+// wave loads all its rows' vectors before storing any, so each wave keeps
+// kRows * 3 KB in flight, and both directions bypass the caches
+// (nontemporal): every byte is touched exactly once.
+constexpr int kRows = 2;
 template <int VB>
 __global__ void __launch_bounds__(256) relayout_rows_kernel(Params p) {
   typedef typename Vec<VB>::T V;
+  constexpr int kU = 3;   // vectors per lane per row pass
   const uint32_t lane = threadIdx.x & 63;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));
   const uint32_t nwaves = gridDim.x * (blockDim.x >> 6);
-  constexpr int kUnroll = 4;
-  for (uint32_t row = wave; row < p.nrows; row += nwaves) {
-    int64_t so, dso;
-    row_offsets(p, row, so, dso);
-    const V *s = reinterpret_cast<const V *>(p.src + so);
-    V *d = reinterpret_cast<V *>(p.dst + dso);
-    for (uint32_t c0 = 0; c0 < p.row_vecs; c0 += 64 * kUnroll) {
-      V buf[kUnroll];
+  for (uint32_t row0 = wave * kRows; row0 < p.nrows; row0 += nwaves * kRows) {
+    for (uint32_t c0 = 0; c0 < p.row_vecs; c0 += 64 * kU) {
+      V buf[kRows][kU];
+      int64_t dso[kRows];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const uint32_t c = c0 + u * 64 + lane;
-        if (c < p.row_vecs) buf[u] = s[c];
+      for (int r = 0; r < kRows; ++r) {
+        int64_t so;
+        row_offsets(p, row0 + r, so, dso[r]);
+        const V *s = reinterpret_cast<const V *>(p.src + so);
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const uint32_t c = c0 + u * 64 + lane;
+          if (row0 + r < p.nrows && c < p.row_vecs) buf[r][u] = __builtin_nontemporal_load(s + c);
+        }
       }
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const uint32_t c = c0 + u * 64 + lane;
-        if (c < p.row_vecs) __builtin_nontemporal_store(buf[u], d + c);
+      for (int r = 0; r < kRows; ++r) {
+        V *d = reinterpret_cast<V *>(p.dst + dso[r]);
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const uint32_t c = c0 + u * 64 + lane;
+          if (row0 + r < p.nrows && c < p.row_vecs) __builtin_nontemporal_store(buf[r][u], d + c);
+        }
       }
     }
   }
@@ -125,7 +136,7 @@ __global__ void __launch_bounds__(256) relayout_items_kernel(Params p, uint32_t 
 template <int VB>
 st_status launch_rows(const Params &p, hipStream_t s) {
   if (p.row_vecs >= 32) {
-    const uint32_t waves = p.nrows;
+    const uint32_t waves = (p.nrows + kRows - 1) / kRows;
     uint32_t blocks = (waves + 3) / 4;
     blocks = std::min<uint32_t>(blocks, 256u * 64u);
     hipLaunchKernelGGL(relayout_rows_kernel<VB>, dim3(blocks), dim3(256), 0, s, p);
