@@ -18,7 +18,11 @@ Sources (page titles as printed on the pages):
         section "V-First compute scheduling": Q and K get RMSNorm and RoPE after
         the linear projection; V gets neither.
   [PF]  PipeFusion technical summary, "Problem definition": attention cost is
-        quadratic in sequence length; sequence parallelism moves Q, K, V.
+        quadratic in sequence length; sequence parallelism (DeepSpeed-Ulysses,
+        Ring-Attention) splits the sequence across devices.
+  [SW]  "Technical Summary: SwiftFusion", sections "Topology-Aware Communication
+        Scheduling" (Ring Attention inside a machine) and "Torus Attention"
+        (attention computed chunk by chunk as the chunks arrive).
 
 Readings where the pages are silent (each is also listed in the design notes):
   R1  RMSNorm is per head over d, eps = 1e-6, gain vector of length d shared by
@@ -31,6 +35,12 @@ Readings where the pages are silent (each is also listed in the design notes):
       s = h * W + w.  base = 10000, positions 0-based and global.
   R4  T is padded to a multiple of N_T with zero frames; keys at t >= t_valid
       are excluded from the temporal softmax (weight exactly 0).
+  R5  Ring and Torus attention ([PF], [SW]) compute attention of the local
+      queries against one key/value chunk at a time and combine the partial
+      results; the pages do not print the combination.  The exact one is used:
+      each chunk yields its normalised output and the log-sum-exp of its
+      scaled scores (natural log; -inf for a chunk with no valid key), and two
+      disjoint chunks combine with weights exp(lse_chunk - lse_union).
 """
 from __future__ import annotations
 
@@ -126,6 +136,65 @@ def attention_probs(q: np.ndarray, k: np.ndarray, scale: float, n_valid: int | N
 def attention(q, k, v, scale: float, n_valid: int | None = None) -> np.ndarray:
     """O = softmax(q k^T * scale) v for one sequence; q, k, v [L, d]."""
     return attention_probs(q, k, scale, n_valid) @ np.asarray(v, np.float64)
+
+
+def attention_lse(q, k, v, scale: float, n_valid: int | None = None):
+    """Attention of q [Lq, d] over one key/value chunk k, v [Lk, d], and its log-sum-exp (R5).
+
+    Returns (o [Lq, d], lse [Lq]): o = softmax(q k^T * scale) v over the chunk's valid keys
+    (j < n_valid), lse_i = log sum_j exp(scale * q_i . k_j) over the same keys.  A chunk with
+    no valid key gives o = 0 and lse = -inf.
+    """
+    q, k, v = (np.asarray(a, np.float64) for a in (q, k, v))
+    nv = k.shape[0] if n_valid is None else min(n_valid, k.shape[0])
+    if nv == 0:
+        return np.zeros((q.shape[0], v.shape[1])), np.full(q.shape[0], -np.inf)
+    z = (q @ k[:nv].T) * scale
+    m = np.max(z, axis=1, keepdims=True)
+    p = np.exp(z - m)
+    l = np.sum(p, axis=1, keepdims=True)
+    return (p / l) @ v[:nv], (m + np.log(l))[:, 0]
+
+
+def merge_partials(o_a, lse_a, o_b, lse_b):
+    """Attention over the union of two disjoint key sets from the two partial results (R5).
+
+    o_* [..., L, d] normalised partial outputs, lse_* [..., L].  The union's softmax mass is
+    exp(lse_a) + exp(lse_b); each part's output is weighted by its share of it.
+    """
+    o_a, o_b = np.asarray(o_a, np.float64), np.asarray(o_b, np.float64)
+    lse_a, lse_b = np.asarray(lse_a, np.float64), np.asarray(lse_b, np.float64)
+    m = np.maximum(lse_a, lse_b)
+    empty = np.isneginf(m)
+    ms = np.where(empty, 0.0, m)
+    wa, wb = np.exp(lse_a - ms), np.exp(lse_b - ms)
+    tot = wa + wb
+    lse = np.where(empty, -np.inf, ms + np.log(np.where(empty, 1.0, tot)))
+    den = np.where(empty, 1.0, tot)[..., None]
+    o = (wa[..., None] * o_a + wb[..., None] * o_b) / den
+    return np.where(empty[..., None], 0.0, o), lse
+
+
+def attn_chunk(q, k, v, scale: float, kv_valid: int | None = None):
+    """Chunk attention over the middle axis: q [outer, Lq, H, d], k, v [outer, Lk, H, d].
+
+    Returns o [outer, Lq, H, d] and lse [outer, H, Lq] (R5); keys j >= kv_valid excluded.
+    """
+    outer, Lq, H, d = q.shape
+    o = np.empty((outer, Lq, H, d))
+    lse = np.empty((outer, H, Lq))
+    for b in range(outer):
+        for h in range(H):
+            o[b, :, h], lse[b, h] = attention_lse(q[b, :, h], k[b, :, h], v[b, :, h], scale, kv_valid)
+    return o, lse
+
+
+def merge_chunks(o_a, lse_a, o_b, lse_b):
+    """merge_partials over [outer, L, H, d] outputs with [outer, H, L] log-sum-exps."""
+    oa = np.moveaxis(np.asarray(o_a, np.float64), 2, 1)   # [outer, H, L, d]
+    ob = np.moveaxis(np.asarray(o_b, np.float64), 2, 1)
+    o, lse = merge_partials(oa, lse_a, ob, lse_b)
+    return np.moveaxis(o, 1, 2), lse
 
 
 def attn_spatial(q, k, v, scale: float) -> np.ndarray:

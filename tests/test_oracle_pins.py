@@ -383,6 +383,94 @@ def test_tiny_config_block_runs_on_synthetic_inputs():
 
 
 # --------------------------------------------------------------------------- #
+# Attention over key chunks and the merge of partial results (R5)             #
+# --------------------------------------------------------------------------- #
+def brute_lse(q, k, scale, n_valid=None):
+    """log sum_j exp(scale * q_i . k_j) with scalar loops and an exact sum."""
+    nv = k.shape[0] if n_valid is None else n_valid
+    out = []
+    for i in range(q.shape[0]):
+        terms = [math.exp(scale * math.fsum(float(q[i, c]) * float(k[j, c]) for c in range(q.shape[1])))
+                 for j in range(nv)]
+        out.append(math.log(math.fsum(terms)) if terms else -math.inf)
+    return np.array(out)
+
+
+@pytest.mark.parametrize("Lq,Lk,nv", [(3, 5, None), (4, 1, None), (2, 6, 4), (5, 7, 1)])
+def test_chunk_attention_and_lse_match_bruteforce(Lq, Lk, nv):
+    r = rng(80 + Lk)
+    q, k, v = r.standard_normal((Lq, 6)), r.standard_normal((Lk, 6)), r.standard_normal((Lk, 6))
+    o, lse = oracle.attention_lse(q, k, v, 0.4, nv)
+    np.testing.assert_allclose(o, brute_attention(q, k, v, 0.4, nv), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, brute_lse(q, k, 0.4, nv), rtol=1e-13, atol=1e-13)
+
+
+def test_lse_closed_forms():
+    r = rng(81)
+    q, k, v = r.standard_normal((3, 5)), r.standard_normal((1, 5)), r.standard_normal((1, 5))
+    _, lse = oracle.attention_lse(q, k, v, 0.7)                       # one key: lse = scale q.k
+    np.testing.assert_allclose(lse, 0.7 * (q @ k[0]), rtol=1e-14)
+    kk = r.standard_normal((9, 5))
+    _, lse = oracle.attention_lse(np.zeros((2, 5)), kk, kk, 0.7)      # q = 0: every score 0 -> log L
+    np.testing.assert_allclose(lse, np.log(9.0), rtol=1e-14)
+    same = np.repeat(k, 6, axis=0)                                   # L equal keys: scale q.k + log L
+    _, lse = oracle.attention_lse(q, same, same, 0.7)
+    np.testing.assert_allclose(lse, 0.7 * (q @ k[0]) + np.log(6.0), rtol=1e-13)
+
+
+@pytest.mark.parametrize("cuts", [(3,), (1, 4), (2, 3, 7, 8)])
+def test_chunked_then_merged_equals_unchunked(cuts):
+    r = rng(82)
+    L, d = 11, 7
+    q, k, v = r.standard_normal((4, d)), r.standard_normal((L, d)), r.standard_normal((L, d))
+    scale = 1.0 / math.sqrt(d)
+    bounds = [0, *cuts, L]
+    parts = [oracle.attention_lse(q, k[a:b], v[a:b], scale) for a, b in zip(bounds, bounds[1:])]
+    o, lse = parts[0]
+    for po, pl in parts[1:]:                                         # left to right
+        o, lse = oracle.merge_partials(o, lse, po, pl)
+    np.testing.assert_allclose(o, brute_attention(q, k, v, scale), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, brute_lse(q, k, scale), rtol=1e-13, atol=1e-13)
+    o2, lse2 = parts[-1]
+    for po, pl in reversed(parts[:-1]):                              # right to left, swapped operands
+        o2, lse2 = oracle.merge_partials(po, pl, o2, lse2)
+    np.testing.assert_allclose(o2, o, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse2, lse, rtol=1e-13, atol=1e-13)
+
+
+def test_merge_with_empty_chunk_is_identity():
+    r = rng(83)
+    q, k, v = r.standard_normal((3, 4)), r.standard_normal((5, 4)), r.standard_normal((5, 4))
+    o, lse = oracle.attention_lse(q, k, v, 0.5)
+    eo, el = oracle.attention_lse(q, k, v, 0.5, n_valid=0)
+    assert np.all(eo == 0.0) and np.all(np.isneginf(el))
+    mo, ml = oracle.merge_partials(o, lse, eo, el)
+    assert np.array_equal(mo, o) and np.array_equal(ml, lse)
+    mo, ml = oracle.merge_partials(eo, el, o, lse)
+    assert np.array_equal(mo, o) and np.array_equal(ml, lse)
+    zo, zl = oracle.merge_partials(eo, el, eo, el)
+    assert np.all(zo == 0.0) and np.all(np.isneginf(zl))
+
+
+def test_chunk_wrappers_are_per_sequence_with_head_major_lse():
+    r = rng(84)
+    q = r.standard_normal((2, 3, 2, 4))
+    k, v = r.standard_normal((2, 5, 2, 4)), r.standard_normal((2, 5, 2, 4))
+    o, lse = oracle.attn_chunk(q, k, v, 0.5, kv_valid=4)
+    assert o.shape == (2, 3, 2, 4) and lse.shape == (2, 2, 3)
+    for b in range(2):
+        for h in range(2):
+            np.testing.assert_allclose(o[b, :, h], brute_attention(q[b, :, h], k[b, :, h], v[b, :, h], 0.5, 4),
+                                       rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(lse[b, h], brute_lse(q[b, :, h], k[b, :, h], 0.5, 4), rtol=1e-13)
+    o1, l1 = oracle.attn_chunk(q, k[:, :2], v[:, :2], 0.5)
+    o2, l2 = oracle.attn_chunk(q, k[:, 2:], v[:, 2:], 0.5, kv_valid=2)
+    mo, ml = oracle.merge_chunks(o1, l1, o2, l2)
+    np.testing.assert_allclose(mo, o, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(ml, lse, rtol=1e-13, atol=1e-13)
+
+
+# --------------------------------------------------------------------------- #
 # Planted mistakes: each must be caught by a pin above                         #
 # --------------------------------------------------------------------------- #
 def test_pins_catch_rope_sign_error():
@@ -410,3 +498,15 @@ def test_pins_catch_norm_over_wrong_axis():
     t[:, 1] *= 100.0
     over_c = t / np.sqrt(np.mean(t.reshape(4, -1) ** 2, axis=-1))[:, None, None]
     assert not np.allclose(over_c[:, 0], oracle.rms_norm_heads(t, np.ones(6), 0.0)[:, 0])
+
+
+def test_pins_catch_wrong_merges():
+    r = rng(73)
+    q, k, v = r.standard_normal((3, 5)), r.standard_normal((8, 5)), r.standard_normal((8, 5))
+    full = brute_attention(q, k, v, 0.5)
+    (oa, la), (ob, lb) = oracle.attention_lse(q, k[:3], v[:3], 0.5), oracle.attention_lse(q, k[3:], v[3:], 0.5)
+    assert not np.allclose((oa + ob) / 2, full)                                  # plain average
+    assert not np.allclose(np.where((la > lb)[:, None], oa, ob), full)           # winner takes all
+    wa, wb = np.exp(la)[:, None], np.exp(lb)[:, None]
+    assert not np.allclose(wa * oa + wb * ob, full)                              # weights not normalised
+    assert np.allclose((wa * oa + wb * ob) / (wa + wb), full)                    # the merge itself
