@@ -154,6 +154,45 @@ st_status st_attn_temporal(const void *q, const void *k, const void *v, int B, i
                            void *stream);
 
 /*
+ * st_attn_chunk -- attention of queries over ONE chunk of keys/values, with the
+ * log-sum-exp of the chunk's scores.  Ring attention (PipeFusion summary,
+ * "Problem definition": sequence parallelism splits the sequence; SwiftFusion,
+ * "Topology-Aware Communication Scheduling") and Torus attention (SwiftFusion,
+ * "Torus Attention") compute attention of the local queries against one
+ * key/value chunk at a time and combine the partial results; st_attn_merge is
+ * the combination.  For every (o, h) and query i:
+ *   out[o, i, h] = softmax_j(scale * q_i . k_j) v_j   over keys j < kv_valid of the chunk
+ *   lse[o, h, i] = log sum_j exp(scale * q_i . k_j)    (natural log, same keys)
+ *
+ *   q        in   [outer, Lq, H, d]
+ *   k, v     in   [outer, Lk, H, d]   (the chunk)
+ *   kv_valid      keys j >= kv_valid of the chunk are excluded; 0 <= kv_valid <= Lk.
+ *                 kv_valid = 0 gives out = 0 and lse = -inf (an empty chunk).
+ *   out      out  [outer, Lq, H, d]   (dtype)
+ *   lse      out  fp32 [outer, H, Lq], 4-byte aligned
+ * Same d support as st_attn_spatial.  Outputs must not overlap the inputs or
+ * each other (ST_EINVAL).  Lq = Lk with kv_valid = Lk is st_attn_spatial plus lse.
+ */
+st_status st_attn_chunk(const void *q, const void *k, const void *v, int64_t outer, int Lq, int Lk, int kv_valid,
+                        int H, int d, float scale, int dtype, void *out, float *lse, void *stream);
+
+/*
+ * st_attn_merge -- the attention result over the union of two disjoint key
+ * chunks, from the two chunk results (st_attn_chunk or earlier merges):
+ *   lse = log(exp(lse_a) + exp(lse_b)),
+ *   out = exp(lse_a - lse) o_a + exp(lse_b - lse) o_b
+ * per (o, i, h), computed in fp32.  A part with lse = -inf (no keys) has weight
+ * 0; two empty parts give out = 0, lse = -inf.
+ *
+ *   o_a, o_b  in   [outer, L, H, d]   (dtype)     lse_a, lse_b  in  fp32 [outer, H, L]
+ *   out       out  [outer, L, H, d]   (dtype)     lse           out fp32 [outer, H, L]
+ * out may be o_a or o_b itself and lse may be lse_a or lse_b itself (a running
+ * merge in place); any other overlap is ST_EINVAL.  d >= 1 (any size).
+ */
+st_status st_attn_merge(const void *o_a, const float *lse_a, const void *o_b, const float *lse_b, int64_t outer, int L,
+                        int H, int d, int dtype, void *out, float *lse, void *stream);
+
+/*
  * st_relayout -- strided N-D copy, the one-GPU form of the spatial <-> temporal
  * redistribution (ScaleFusion review, "Technical architecture", execution flow)
  * and of the blocked rearranges and slice gathers/scatters of the algorithm

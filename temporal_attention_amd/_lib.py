@@ -23,11 +23,12 @@ ST_ROPE_NONE, ST_ROPE_1D, ST_ROPE_2D = 0, 1, 2
 # Every entry point declared in include/st.h.
 EXPORTS = (
     "st_status_str", "st_rope_table_floats", "st_rope_table", "st_qkv_norm_rope", "st_out_proj",
-    "st_attn_spatial", "st_attn_temporal", "st_relayout", "st_block_sliced", "st_block_sliced_workspace",
+    "st_attn_spatial", "st_attn_temporal", "st_attn_chunk", "st_attn_merge", "st_relayout", "st_block_sliced",
+    "st_block_sliced_workspace",
 )
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m temporal_attention_amd.build`")
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python temporal_attention_amd/build.py`")
 
 # torch ships its own HIP runtime.  libst.so must bind to that same runtime
 # (device memory and streams come from torch), so torch is loaded first.
@@ -60,6 +61,8 @@ _SIGS = {
     "st_out_proj": (_i, [_p, _i64, _i, _p, _i, _i, _p, _p]),
     "st_attn_spatial": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p, _p]),
     "st_attn_temporal": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p, _p]),
+    "st_attn_chunk": (_i, [_p, _p, _p, _i64, _i, _i, _i, _i, _i, _f, _i, _p, _p, _p]),
+    "st_attn_merge": (_i, [_p, _p, _p, _p, _i64, _i, _i, _i, _i, _p, _p, _p]),
     "st_relayout": (_i, [_p, C.POINTER(C.c_int64), _p, C.POINTER(C.c_int64), C.POINTER(C.c_int64), _i, _i, _p]),
     "st_block_sliced": (_i, [_p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, C.POINTER(st_layer_weights),
                              C.POINTER(st_layer_weights), _f, _f, _i, _p, _p, _sz, _p]),
@@ -129,6 +132,16 @@ def st_attn_spatial(q, k, v, B, T, S, H, d, scale, dtype, out, stream=None):
 def st_attn_temporal(q, k, v, B, S, T, t_valid, H, d, scale, dtype, out, stream=None):
     _check("st_attn_temporal", lib.st_attn_temporal(_ptr(q), _ptr(k), _ptr(v), B, S, T, t_valid, H, d, scale, dtype,
                                                     _ptr(out), _stream(stream)))
+
+
+def st_attn_chunk(q, k, v, outer, Lq, Lk, kv_valid, H, d, scale, dtype, out, lse, stream=None):
+    _check("st_attn_chunk", lib.st_attn_chunk(_ptr(q), _ptr(k), _ptr(v), outer, Lq, Lk, kv_valid, H, d, scale, dtype,
+                                              _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def st_attn_merge(o_a, lse_a, o_b, lse_b, outer, L, H, d, dtype, out, lse, stream=None):
+    _check("st_attn_merge", lib.st_attn_merge(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), outer, L, H, d, dtype,
+                                              _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def _i64arr(vals):

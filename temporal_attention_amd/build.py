@@ -1,6 +1,9 @@
 """Build libst.so (HIP, gfx950) in-tree: temporal_attention_amd/libst.so.
 
-    python -m temporal_attention_amd.build      # or build() from Python
+    python temporal_attention_amd/build.py      # or build() from __graft_entry__
+
+(Run it as a script, not as `-m temporal_attention_amd.build`: importing the
+package loads the existing libst.so, which may predate the sources.)
 
 Each .hip source compiles to an object under temporal_attention_amd/_build/
 (in parallel), then one shared library is linked next to this file.

@@ -39,9 +39,10 @@ namespace {
 struct AttnArgs {
   const u16 *q, *k, *v;
   u16 *o;
+  float *lse;          // optional [outer, H, L]: natural log-sum-exp of the scaled scores per query
   int64_t outer;
-  int L, n_valid, H;
-  float c;   // scale * log2(e)
+  int L, Lk, n_valid, H;   // L queries, Lk keys per sequence (equal except for chunk attention)
+  float c;             // scale * log2(e)
 };
 
 template <int D>
@@ -428,17 +429,18 @@ __global__ void __launch_bounds__(64 * kLongWaves, 8 / kLongWaves) attn_long_ker
   const int h = (int)(seq % (uint32_t)a.H);
   const int64_t outer = seq / (uint32_t)a.H;
   const int64_t rs = (int64_t)a.H * D;                  // row stride (elements)
-  const int64_t base = outer * a.L * rs + (int64_t)h * D;
-  const u16 *qp = a.q + base, *kp = a.k + base, *vp = a.v + base;
-  u16 *op = a.o + base;
+  const int64_t qbase = outer * a.L * rs + (int64_t)h * D;
+  const int64_t kvbase = outer * a.Lk * rs + (int64_t)h * D;
+  const u16 *qp = a.q + qbase, *kp = a.k + kvbase, *vp = a.v + kvbase;
+  u16 *op = a.o + qbase;
 
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
-  const int L = a.L;
+  const int L = a.L, Lk = a.Lk;
 
   W w;
   w.c = a.c;
-  w.nv = min(L, a.n_valid);
+  w.nv = min(Lk, a.n_valid);
   w.l32 = lane & 31;
   w.g = lane >> 5;
   w.q16 = lane & 15;
@@ -515,11 +517,11 @@ __global__ void __launch_bounds__(64 * kLongWaves, 8 / kLongWaves) attn_long_ker
   const bool partial = (w.nv & 31) != 0;
   LongDma<D> dma;
   dma.init(rs, lane, wave);
-  if (ntl == 0) return;   // whole workgroup: n_valid is uniform
-  dma.issue(lds, 0, kp, vp, rs, L, lane, wave);
+  if (ntl == 0) return;   // whole workgroup: n_valid is uniform (the host never launches with none)
+  dma.issue(lds, 0, kp, vp, rs, Lk, lane, wave);
   wait_vmem();
   __syncthreads();
-  if (ntl > 1) dma.issue(lds + C::STAGE, C::KB, kp, vp, rs, L, lane, wave);
+  if (ntl > 1) dma.issue(lds + C::STAGE, C::KB, kp, vp, rs, Lk, lane, wave);
 
   f32x16 sb[2][NT];
   {
@@ -540,7 +542,7 @@ __global__ void __launch_bounds__(64 * kLongWaves, 8 / kLongWaves) attn_long_ker
     w.template step<true, 0>(sb, Vs, Ks + 32 * D, 2 * kt + 1, partial && 2 * kt + 1 == nu - 1);
     wait_vmem();
     __syncthreads();
-    if (kt + 2 < ntl) dma.issue(lds + st2 * C::STAGE, (kt + 2) * C::KB, kp, vp, rs, L, lane, wave);
+    if (kt + 2 < ntl) dma.issue(lds + st2 * C::STAGE, (kt + 2) * C::KB, kp, vp, rs, Lk, lane, wave);
     w.template step<true, 1>(sb, Vs + 32 * D, lds + st1 * C::STAGE, 2 * kt + 2, partial && 2 * kt + 2 == nu - 1);
     st = st1;
   }
@@ -572,6 +574,11 @@ __global__ void __launch_bounds__(64 * kLongWaves, 8 / kLongWaves) attn_long_ker
     }
     const float inv = 1.0f / l;
     const int qi = q0 + nt * 32 + w.l32;
+    if (a.lse && qi < L && w.g == 0) {
+      // sum_j exp(scale s_j) = 2^M * l, M = the running max in scaled log2 units
+      const float M = W::FOLD ? w.m[nt] : w.m[nt] * w.c;
+      a.lse[(outer * a.H + h) * (int64_t)L + qi] = (M + log2f(l)) * 0.69314718055994531f;
+    }
     if (qi < L) {
       u16 *orow = op + (int64_t)qi * rs;
 #pragma unroll
@@ -800,15 +807,17 @@ st_status launch_short(const AttnArgs &a, hipStream_t s) {
   return launch_status();
 }
 
-AttnArgs make_args(const void *q, const void *k, const void *v, int64_t outer, int L, int n_valid, int H,
-                   float scale, void *out) {
+AttnArgs make_args(const void *q, const void *k, const void *v, int64_t outer, int L, int Lk, int n_valid, int H,
+                   float scale, void *out, float *lse) {
   AttnArgs a;
   a.q = static_cast<const u16 *>(q);
   a.k = static_cast<const u16 *>(k);
   a.v = static_cast<const u16 *>(v);
   a.o = static_cast<u16 *>(out);
+  a.lse = lse;
   a.outer = outer;
   a.L = L;
+  a.Lk = Lk;
   a.n_valid = n_valid;
   a.H = H;
   a.c = (float)((double)scale * 1.4426950408889634);
@@ -822,8 +831,13 @@ bool attn_short_supported(int L, int d) { return L <= 64 && (d == 64 || d == 72)
 
 st_status launch_attn_bf16(const void *q, const void *k, const void *v, int64_t outer, int L, int n_valid, int H,
                            int d, float scale, void *out, hipStream_t s) {
-  if (outer == 0 || L == 0) return ST_OK;
-  const AttnArgs a = make_args(q, k, v, outer, L, n_valid, H, scale, out);
+  return launch_attn_chunk_bf16(q, k, v, outer, L, L, n_valid, H, d, scale, out, nullptr, s);
+}
+
+st_status launch_attn_chunk_bf16(const void *q, const void *k, const void *v, int64_t outer, int Lq, int Lk,
+                                 int n_valid, int H, int d, float scale, void *out, float *lse, hipStream_t s) {
+  if (outer == 0 || Lq == 0) return ST_OK;
+  const AttnArgs a = make_args(q, k, v, outer, Lq, Lk, n_valid, H, scale, out, lse);
   switch (d) {
     case 72: return launch_long<72, 2>(a, s);
     case 64: return launch_long<64, 2>(a, s);
@@ -835,7 +849,7 @@ st_status launch_attn_bf16(const void *q, const void *k, const void *v, int64_t 
 st_status launch_attn_short_bf16(const void *q, const void *k, const void *v, int64_t outer, int L, int n_valid,
                                  int H, int d, float scale, void *out, hipStream_t s) {
   if (outer == 0 || L == 0) return ST_OK;
-  const AttnArgs a = make_args(q, k, v, outer, L, n_valid, H, scale, out);
+  const AttnArgs a = make_args(q, k, v, outer, L, L, n_valid, H, scale, out, nullptr);
   if (d == 72) return L <= 32 ? launch_short<72, 1>(a, s) : launch_short<72, 2>(a, s);
   if (d == 64) return L <= 32 ? launch_short<64, 1>(a, s) : launch_short<64, 2>(a, s);
   return ST_EUNSUPPORTED;

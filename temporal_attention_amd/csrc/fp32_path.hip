@@ -78,8 +78,10 @@ __global__ void norm_rope_f32_kernel(int64_t rows, int H, int d, float *q, float
 }
 
 // One thread per (outer, head, query): two passes over the keys.
-__global__ void attn_f32_kernel(const float *q, const float *k, const float *v, int64_t outer, int L, int nv,
-                                int H, int d, float scale, float *o) {
+// One thread per (sequence, head, query); L queries over Lk keys, the first nv
+// of them valid (nv >= 1).  lse (optional, [outer, H, L]) gets m + log(l).
+__global__ void attn_f32_kernel(const float *q, const float *k, const float *v, int64_t outer, int L, int Lk, int nv,
+                                int H, int d, float scale, float *o, float *lse) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= outer * H * L) return;
   const int qi = (int)(i % L);
@@ -88,10 +90,11 @@ __global__ void attn_f32_kernel(const float *q, const float *k, const float *v, 
   const int64_t ou = oh / H;
   const int64_t rs = (int64_t)H * d;
   const int64_t base = ou * L * rs + (int64_t)h * d;
+  const int64_t kbase = ou * Lk * rs + (int64_t)h * d;
   const float *qr = q + base + qi * rs;
   float m = -INFINITY;
   for (int j = 0; j < nv; ++j) {
-    const float *kr = k + base + j * rs;
+    const float *kr = k + kbase + j * rs;
     float s = 0.f;
     for (int c = 0; c < d; ++c) s = fmaf(qr[c], kr[c], s);
     m = fmaxf(m, s * scale);
@@ -100,8 +103,8 @@ __global__ void attn_f32_kernel(const float *q, const float *k, const float *v, 
   for (int c = 0; c < d; ++c) acc[c] = 0.f;
   float l = 0.f;
   for (int j = 0; j < nv; ++j) {
-    const float *kr = k + base + j * rs;
-    const float *vr = v + base + j * rs;
+    const float *kr = k + kbase + j * rs;
+    const float *vr = v + kbase + j * rs;
     float s = 0.f;
     for (int c = 0; c < d; ++c) s = fmaf(qr[c], kr[c], s);
     const float p = expf(s * scale - m);
@@ -110,6 +113,7 @@ __global__ void attn_f32_kernel(const float *q, const float *k, const float *v, 
   }
   float *orow = o + base + qi * rs;
   for (int c = 0; c < d; ++c) orow[c] = acc[c] / l;
+  if (lse) lse[oh * L + qi] = m + logf(l);
 }
 
 inline unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
@@ -142,8 +146,18 @@ st_status launch_attn_f32(const float *q, const float *k, const float *v, int64_
   const int64_t n = outer * H * L;
   if (n == 0) return ST_OK;
   if (blocks_for(n) >= (1u << 31)) return ST_EUNSUPPORTED;
-  hipLaunchKernelGGL(attn_f32_kernel, dim3(blocks_for(n)), dim3(256), 0, s, q, k, v, outer, L, min(n_valid, L), H,
-                     d, scale, out);
+  hipLaunchKernelGGL(attn_f32_kernel, dim3(blocks_for(n)), dim3(256), 0, s, q, k, v, outer, L, L, min(n_valid, L), H,
+                     d, scale, out, (float *)nullptr);
+  return launch_status();
+}
+
+st_status launch_attn_chunk_f32(const float *q, const float *k, const float *v, int64_t outer, int Lq, int Lk,
+                                int n_valid, int H, int d, float scale, float *out, float *lse, hipStream_t s) {
+  const int64_t n = outer * H * Lq;
+  if (n == 0) return ST_OK;
+  if (blocks_for(n) >= (1u << 31)) return ST_EUNSUPPORTED;
+  hipLaunchKernelGGL(attn_f32_kernel, dim3(blocks_for(n)), dim3(256), 0, s, q, k, v, outer, Lq, Lk,
+                     min(n_valid, Lk), H, d, scale, out, lse);
   return launch_status();
 }
 

@@ -218,6 +218,53 @@ st_status st_attn_temporal(const void *q, const void *k, const void *v, int B, i
   return attn_common(q, k, v, (int64_t)B * S, T, t_valid, H, d, scale, dtype, out, true, stream);
 }
 
+st_status st_attn_chunk(const void *q, const void *k, const void *v, int64_t outer, int Lq, int Lk, int kv_valid,
+                        int H, int d, float scale, int dtype, void *out, float *lse, void *stream) {
+  if (!dtype_ok(dtype)) return ST_EINVAL;
+  if (!q || !k || !v || !out || !lse || H < 1 || outer < 0 || Lq < 0 || Lk < 0) return ST_EINVAL;
+  if (kv_valid < 0 || kv_valid > Lk || d < 2 || d % 2) return ST_EINVAL;
+  if (!(scale > 0.f) || !isfinite(scale)) return ST_EINVAL;
+  if (!head_dim_ok(d, dtype, ST_ROPE_NONE)) return ST_EUNSUPPORTED;
+  if (outer >= (1ll << 40) || Lq >= (1 << 30) || Lk >= (1 << 30)) return ST_EUNSUPPORTED;
+  for (const void *p : {q, k, v, (const void *)out})
+    if (!aligned16(p)) return ST_EALIGN;
+  if ((uintptr_t)lse % 4) return ST_EALIGN;
+  const int64_t e = (int64_t)esize(dtype);
+  const Range ro = rng(out, outer * Lq * H * d * e), rl = rng(lse, outer * H * Lq * 4);
+  const Range rq = rng(q, outer * Lq * H * d * e), rk = rng(k, outer * Lk * H * d * e), rv = rng(v, outer * Lk * H * d * e);
+  for (const Range &in : {rq, rk, rv})
+    if (overlap(ro, in) || overlap(rl, in)) return ST_EINVAL;
+  if (overlap(ro, rl)) return ST_EINVAL;
+  if (outer == 0 || Lq == 0) return ST_OK;
+  hipStream_t s = (hipStream_t)stream;
+  if (kv_valid == 0) return launch_attn_empty(out, lse, outer, Lq, H, d, (int)e, s);
+  if (dtype == ST_F32)
+    return launch_attn_chunk_f32((const float *)q, (const float *)k, (const float *)v, outer, Lq, Lk, kv_valid, H, d,
+                                 scale, (float *)out, lse, s);
+  return launch_attn_chunk_bf16(q, k, v, outer, Lq, Lk, kv_valid, H, d, scale, out, lse, s);
+}
+
+st_status st_attn_merge(const void *o_a, const float *lse_a, const void *o_b, const float *lse_b, int64_t outer, int L,
+                        int H, int d, int dtype, void *out, float *lse, void *stream) {
+  if (!dtype_ok(dtype)) return ST_EINVAL;
+  if (!o_a || !lse_a || !o_b || !lse_b || !out || !lse || outer < 0 || L < 0 || H < 1 || d < 1) return ST_EINVAL;
+  if (outer >= (1ll << 40) || L >= (1 << 30) || d > 4096) return ST_EUNSUPPORTED;
+  for (const void *p : {o_a, o_b, (const void *)out})
+    if (!aligned16(p)) return ST_EALIGN;
+  for (const float *p : {lse_a, lse_b, (const float *)lse})
+    if ((uintptr_t)p % 4) return ST_EALIGN;
+  const int64_t ob = outer * L * H * d * (int64_t)esize(dtype), lb = outer * H * L * 4;
+  const Range ro = rng(out, ob), rl = rng(lse, lb);
+  const Range ra = rng(o_a, ob), rb = rng(o_b, ob), rla = rng(lse_a, lb), rlb = rng(lse_b, lb);
+  // in place on either input is fine (each row is read before it is written); partial overlap is not
+  if ((overlap(ro, ra) && out != o_a) || (overlap(ro, rb) && out != o_b)) return ST_EINVAL;
+  if ((overlap(rl, rla) && lse != lse_a) || (overlap(rl, rlb) && lse != lse_b)) return ST_EINVAL;
+  for (const Range &x : {rl, rla, rlb})
+    if (overlap(ro, x) || overlap(ra, x) || overlap(rb, x)) return ST_EINVAL;
+  if (outer == 0 || L == 0) return ST_OK;
+  return launch_attn_merge(o_a, lse_a, o_b, lse_b, outer, L, H, d, (int)esize(dtype), out, lse, (hipStream_t)stream);
+}
+
 st_status st_relayout(const void *src, const int64_t *src_strides, void *dst, const int64_t *dst_strides,
                       const int64_t *dims, int ndim, int elem_bytes, void *stream) {
   if (!src || !dst || !src_strides || !dst_strides || !dims) return ST_EINVAL;

@@ -77,6 +77,17 @@ st_status launch_attn_short_bf16(const void *q, const void *k, const void *v, in
                                  int n_valid, int H, int d, float scale, void *out, hipStream_t s);
 st_status launch_attn_f32(const float *q, const float *k, const float *v, int64_t outer, int L, int n_valid,
                           int H, int d, float scale, float *out, hipStream_t s);
+// Attention of Lq queries over a chunk of Lk keys (keys j >= n_valid masked, n_valid >= 1), optionally
+// writing the natural log-sum-exp of the scaled scores per query to lse [outer, H, Lq].
+st_status launch_attn_chunk_bf16(const void *q, const void *k, const void *v, int64_t outer, int Lq, int Lk,
+                                 int n_valid, int H, int d, float scale, void *out, float *lse, hipStream_t s);
+st_status launch_attn_chunk_f32(const float *q, const float *k, const float *v, int64_t outer, int Lq, int Lk,
+                                int n_valid, int H, int d, float scale, float *out, float *lse, hipStream_t s);
+// o = 0 and lse = -inf for a chunk without valid keys; elem_bytes 2 or 4.
+st_status launch_attn_empty(void *o, float *lse, int64_t outer, int L, int H, int d, int elem_bytes, hipStream_t s);
+// Merge of two chunk results over [outer, L, H, d] with [outer, H, L] log-sum-exps (in place allowed).
+st_status launch_attn_merge(const void *o_a, const float *lse_a, const void *o_b, const float *lse_b, int64_t outer,
+                            int L, int H, int d, int elem_bytes, void *o, float *lse, hipStream_t s);
 
 bool attn_bf16_supported(int d);
 bool attn_short_supported(int L, int d);

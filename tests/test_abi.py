@@ -121,6 +121,56 @@ def test_attn_temporal_validation(t_valid, want):
     assert code(st.st_attn_temporal, P, P2, P3, 1, 8160, 52, t_valid, 16, 72, 0.1, st.ST_BF16, BIG) == want
 
 
+def chunk_args(**kw):
+    a = dict(q=P, k=P2, v=P3, outer=51, Lq=100, Lk=64, kv_valid=64, H=16, d=72, scale=0.1, dtype=st.ST_BF16, out=BIG,
+             lse=2 * BIG)
+    a.update(kw)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), st.ST_EINVAL),
+    (dict(lse=None), st.ST_EINVAL),
+    (dict(kv_valid=-1), st.ST_EINVAL),
+    (dict(kv_valid=65), st.ST_EINVAL),               # more valid keys than the chunk holds
+    (dict(Lk=-1), st.ST_EINVAL),
+    (dict(outer=-1), st.ST_EINVAL),
+    (dict(scale=0.0), st.ST_EINVAL),
+    (dict(dtype=5), st.ST_EINVAL),
+    (dict(d=96), st.ST_EUNSUPPORTED),
+    (dict(out=P2), st.ST_EINVAL),                    # out aliases k
+    (dict(lse=P3 + 64), st.ST_EINVAL),               # lse overlaps v
+    (dict(lse=BIG + 128), st.ST_EINVAL),             # lse overlaps out
+    (dict(out=BIG + 4), st.ST_EALIGN),
+    (dict(lse=2 * BIG + 2), st.ST_EALIGN),
+])
+def test_attn_chunk_validation(kw, want):
+    assert code(st.st_attn_chunk, *chunk_args(**kw)) == want
+
+
+def merge_args(**kw):
+    a = dict(o_a=P, lse_a=P2, o_b=P3, lse_b=P4, outer=51, L=100, H=16, d=72, dtype=st.ST_BF16, out=BIG, lse=2 * BIG)
+    a.update(kw)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(o_a=None), st.ST_EINVAL),
+    (dict(lse_b=None), st.ST_EINVAL),
+    (dict(H=0), st.ST_EINVAL),
+    (dict(d=0), st.ST_EINVAL),
+    (dict(dtype=9), st.ST_EINVAL),
+    (dict(out=P + 32), st.ST_EINVAL),                # partial overlap with o_a (in place must be exact)
+    (dict(lse=P2 + 4), st.ST_EINVAL),                # partial overlap with lse_a
+    (dict(lse=BIG + 64), st.ST_EINVAL),              # lse inside out
+    (dict(out=P2), st.ST_EINVAL),                    # out over lse_a
+    (dict(out=BIG + 8), st.ST_EALIGN),
+    (dict(lse=2 * BIG + 1), st.ST_EALIGN),
+])
+def test_attn_merge_validation(kw, want):
+    assert code(st.st_attn_merge, *merge_args(**kw)) == want
+
+
 def test_relayout_validation():
     dims, s1, s2 = [2, 3, 4], [12, 4, 1], [12, 1, 3]
     assert code(st.st_relayout, None, s1, BIG, s2, dims, 3, 2) == st.ST_EINVAL

@@ -1,0 +1,179 @@
+"""Chunk attention with log-sum-exp and the merge of chunk results, on the GPU against the fp64 oracle.
+
+Ring and Torus attention compute attention over one key/value chunk at a time
+and merge the partial results; on one GPU the identity that pins this is
+chunked-then-merged == unchunked.  Inputs are seeded (st_synth), identical
+bytes on both sides.
+
+Tolerances: outputs use the bf16 / fp32 bars of the other kernels.  The bf16
+log-sum-exp is fp32 arithmetic on bf16 operands, and for d = 72 the kernel
+rounds scale*log2(e)*q to bf16 once more before the product (up to 2^-8
+relative per element, round to nearest).  The resulting score error is a
+signed sum of d such terms and grows with the score magnitude, so the bar is
+relative: |lse - lse_ref| <= max(2e-2, 2^-7 * max|lse_ref|) over a call (about
+3-4 standard deviations of that sum at these inputs).  The fp32 path is held to
+1e-4 absolute.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import st_synth
+from helpers import assert_close, empty, f64, to_dev, torch
+
+pytestmark = pytest.mark.gpu
+
+t_ = torch()
+if not t_.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import temporal_attention_amd as st  # noqa: E402
+
+BF, F32 = st.ST_BF16, st.ST_F32
+LSE_BF16, LSE_F32 = 2e-2, 1e-4
+
+
+def lse_tol(ref, dt):
+    if dt != BF:
+        return LSE_F32
+    return max(LSE_BF16, 2.0 ** -7 * float(np.max(np.abs(ref))) if ref.size else 0.0)
+
+
+def sync():
+    t_.cuda.synchronize()
+
+
+def tensors(shape_q, shape_kv, seed, dt, q_std=1.0):
+    sd = "bf16" if dt == BF else "f32"
+    return (st_synth.randn(shape_q, seed, std=q_std, dtype=sd), st_synth.randn(shape_kv, seed + 1, dtype=sd),
+            st_synth.randn(shape_kv, seed + 2, dtype=sd))
+
+
+def lse_buf(outer, H, L):
+    return t_.empty((outer, H, L), dtype=t_.float32, device="cuda")
+
+
+def check_lse(got, ref, dt, what="lse"):
+    got = got.cpu().numpy().astype(np.float64)
+    assert np.array_equal(np.isneginf(got), np.isneginf(ref)), f"{what}: -inf pattern differs"
+    fin = np.isfinite(ref)
+    err = float(np.max(np.abs(got[fin] - ref[fin]))) if fin.any() else 0.0
+    assert err <= lse_tol(ref[fin], dt), f"{what}: max_abs={err:.3e}"
+
+
+CHUNK_CASES = [
+    # outer, Lq, Lk, kv_valid, H, d, q_std, dtype
+    (3, 300, 500, 500, 2, 72, 1.0, BF),     # fewer queries than keys
+    (2, 257, 100, 77, 3, 72, 3.0, BF),      # masked tail, peaked softmax (many rescales)
+    (1, 64, 1, 1, 2, 72, 1.0, BF),          # one key
+    (2, 100, 130, 130, 2, 128, 1.0, BF),
+    (2, 70, 200, 150, 2, 64, 2.0, BF),
+    (2, 33, 40, 35, 2, 64, 1.0, F32),
+    (2, 50, 20, 0, 2, 72, 1.0, BF),         # empty chunk: out 0, lse -inf
+    (2, 10, 5, 0, 2, 64, 1.0, F32),
+]
+
+
+@pytest.mark.parametrize("outer,Lq,Lk,kv_valid,H,d,q_std,dt", CHUNK_CASES)
+def test_attn_chunk_matches_oracle(outer, Lq, Lk, kv_valid, H, d, q_std, dt):
+    q, k, v = tensors((outer, Lq, H, d), (outer, Lk, H, d), 700 + Lq + Lk + d, dt, q_std)
+    out, lse = empty((outer, Lq, H, d), dt == BF), lse_buf(outer, H, Lq)
+    scale = 1.0 / math.sqrt(d)
+    st.st_attn_chunk(to_dev(q), to_dev(k), to_dev(v), outer, Lq, Lk, kv_valid, H, d, scale, dt, out, lse)
+    sync()
+    ro, rl = oracle.attn_chunk(f64(q), f64(k), f64(v), scale, kv_valid)
+    if kv_valid == 0:
+        assert np.all(f64(out) == 0.0)
+    else:
+        assert_close(f64(out), ro, bf16=dt == BF, what="O")
+    check_lse(lse, rl, dt)
+
+
+def test_attn_chunk_without_lse_path_matches_spatial_kernel():
+    # Lq = Lk, all keys valid: the chunk entry point is spatial attention plus lse, bit for bit
+    outer, L, H, d = 2, 333, 2, 72
+    q, k, v = (to_dev(a) for a in tensors((outer, L, H, d), (outer, L, H, d), 901, BF))
+    a, b = empty((outer, L, H, d)), empty((outer, L, H, d))
+    st.st_attn_chunk(q, k, v, outer, L, L, L, H, d, 1 / math.sqrt(d), BF, a, lse_buf(outer, H, L))
+    st.st_attn_spatial(q, k, v, 1, outer, L, H, d, 1 / math.sqrt(d), BF, b)
+    sync()
+    assert t_.equal(a, b)
+
+
+@pytest.mark.parametrize("dt,d,cuts,valid", [
+    (BF, 72, (300, 301), 950),        # three chunks, one of a single key, masked tail
+    (BF, 128, (64, 500), 700),
+    (BF, 64, (1,), 1000),
+    (F32, 64, (100, 450), 999),
+])
+def test_chunked_then_merged_equals_unchunked(dt, d, cuts, valid):
+    outer, L, H = 2, 1000, 2
+    q, k, v = tensors((outer, L, H, d), (outer, L, H, d), 1300 + d + len(cuts), dt, 2.0)
+    scale = 1.0 / math.sqrt(d)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    bounds = [0, *cuts, L]
+    acc_o, acc_l = empty((outer, L, H, d), dt == BF), lse_buf(outer, H, L)
+    part_o, part_l = empty((outer, L, H, d), dt == BF), lse_buf(outer, H, L)
+    for i, (a, b) in enumerate(zip(bounds, bounds[1:])):
+        kc, vc = kd[:, a:b].contiguous(), vd[:, a:b].contiguous()
+        nv = max(0, min(b, valid) - a)
+        dst_o, dst_l = (acc_o, acc_l) if i == 0 else (part_o, part_l)
+        st.st_attn_chunk(qd, kc, vc, outer, L, b - a, nv, H, d, scale, dt, dst_o, dst_l)
+        if i > 0:   # running merge, in place into the accumulator
+            st.st_attn_merge(acc_o, acc_l, part_o, part_l, outer, L, H, d, dt, acc_o, acc_l)
+    sync()
+    ro, rl = oracle.attn_chunk(f64(q), f64(k), f64(v), scale, valid)
+    assert_close(f64(acc_o), ro, bf16=dt == BF, what="merged O")
+    check_lse(acc_l, rl, dt, "merged lse")
+
+
+@pytest.mark.parametrize("dt,d", [(BF, 72), (F32, 64), (BF, 5)])
+def test_merge_matches_oracle_including_empty_parts(dt, d):
+    outer, L, H = 3, 77, 4
+    sd = "bf16" if dt == BF else "f32"
+    oa, ob = st_synth.randn((outer, L, H, d), 1500 + d, dtype=sd), st_synth.randn((outer, L, H, d), 1501 + d, dtype=sd)
+    r = np.random.default_rng(1502 + d)
+    la = r.normal(0.0, 4.0, (outer, H, L)).astype(np.float32)
+    lb = r.normal(0.0, 4.0, (outer, H, L)).astype(np.float32)
+    la[0, 0, :5] = -np.inf            # part a empty for some rows
+    lb[1, 2, 3:9] = -np.inf           # part b empty for others
+    la[2, 1, 10] = lb[2, 1, 10] = -np.inf   # both empty
+    ta, tb = t_.from_numpy(la).cuda(), t_.from_numpy(lb).cuda()
+    out, lse = empty((outer, L, H, d), dt == BF), lse_buf(outer, H, L)
+    st.st_attn_merge(to_dev(oa), ta, to_dev(ob), tb, outer, L, H, d, dt, out, lse)
+    sync()
+    ro, rl = oracle.merge_chunks(f64(oa), la.astype(np.float64), f64(ob), lb.astype(np.float64))
+    assert_close(f64(out), ro, bf16=dt == BF, what="merge O")
+    got = lse.cpu().numpy().astype(np.float64)
+    assert np.array_equal(np.isneginf(got), np.isneginf(rl))
+    fin = np.isfinite(rl)
+    np.testing.assert_allclose(got[fin], rl[fin], rtol=1e-6, atol=1e-6)
+    assert np.all(f64(out)[2, 10, 1] == 0.0)
+
+
+def test_chunked_merge_at_1080p_frame_shape_sampled():
+    # one 1080p frame (8160 patches x 16 heads x 72) in three uneven key chunks, merged;
+    # checked against the oracle on a seeded sample of queries of every head
+    L, H, d, outer = 8160, 16, 72, 1
+    q, k, v = tensors((outer, L, H, d), (outer, L, H, d), 1700, BF)
+    scale = 1.0 / math.sqrt(d)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    bounds = [0, 2000, 2001, L]
+    acc_o, acc_l = empty((outer, L, H, d)), lse_buf(outer, H, L)
+    part_o, part_l = empty((outer, L, H, d)), lse_buf(outer, H, L)
+    for i, (a, b) in enumerate(zip(bounds, bounds[1:])):
+        dst_o, dst_l = (acc_o, acc_l) if i == 0 else (part_o, part_l)
+        st.st_attn_chunk(qd, kd[:, a:b].contiguous(), vd[:, a:b].contiguous(), outer, L, b - a, b - a, H, d, scale,
+                         BF, dst_o, dst_l)
+        if i > 0:
+            st.st_attn_merge(acc_o, acc_l, part_o, part_l, outer, L, H, d, BF, acc_o, acc_l)
+    sync()
+    rows = np.random.default_rng(1701).choice(L, 48, replace=False)
+    got_o, got_l = f64(acc_o), acc_l.cpu().numpy().astype(np.float64)
+    qf, kf, vf = f64(q), f64(k), f64(v)
+    for h in range(H):
+        ro, rl = oracle.attention_lse(qf[0, rows, h], kf[0, :, h], vf[0, :, h], scale)
+        assert_close(got_o[0, rows, h], ro, what=f"head {h}")
+        assert np.max(np.abs(got_l[0, h, rows] - rl)) <= lse_tol(rl, BF)
