@@ -117,6 +117,55 @@ def cpu_baseline(inp, cfg, budget_s=20.0):
             "seconds": round(dt, 2), "host_cores_visible": len(os.sched_getaffinity(0))}
 
 
+def time_chunked_attention(lp, B, T, S, H, d, reps, stream, n_chunks=4):
+    """Spatial attention of the step's q, k, v as a 4-way key split, the work of one GPU of a
+    4-way ring: st_attn_chunk per key chunk (with log-sum-exp), folded together by three
+    in-place st_attn_merge calls; against one st_attn_chunk over all keys."""
+    import torch
+
+    import temporal_attention_amd as st
+
+    outer, scale = B * T, 1.0 / math.sqrt(d)
+    bounds = [S * i // n_chunks for i in range(n_chunks + 1)]
+    kc = [lp.k.view(outer, S, H, d)[:, a:b].contiguous() for a, b in zip(bounds, bounds[1:])]
+    vc = [lp.v.view(outer, S, H, d)[:, a:b].contiguous() for a, b in zip(bounds, bounds[1:])]
+    acc, part = torch.empty_like(lp.o), torch.empty_like(lp.o)
+    lse_acc = torch.empty((outer, H, S), dtype=torch.float32, device="cuda")
+    lse_part = torch.empty_like(lse_acc)
+    times = {}
+
+    def whole():
+        st.st_attn_chunk(lp.q, lp.k, lp.v, outer, S, S, S, H, d, scale, st.ST_BF16, acc, lse_acc)
+
+    def chunked():
+        for i, (a, b) in enumerate(zip(bounds, bounds[1:])):
+            dst, dl = (acc, lse_acc) if i == 0 else (part, lse_part)
+            st.st_attn_chunk(lp.q, kc[i], vc[i], outer, S, b - a, b - a, H, d, scale, st.ST_BF16, dst, dl)
+            if i:
+                st.st_attn_merge(acc, lse_acc, part, lse_part, outer, S, H, d, st.ST_BF16, acc, lse_acc)
+
+    def merge_only():
+        st.st_attn_merge(acc, lse_acc, part, lse_part, outer, S, H, d, st.ST_BF16, acc, lse_acc)
+
+    for name, fn in (("whole", whole), ("chunked", chunked), ("merge", merge_only)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times[name] = e0.elapsed_time(e1) / reps
+    fl = 4.0 * S * S * d * H * outer
+    merge_bytes = outer * S * H * (3 * d * 2 + 3 * 4)     # read two rows + lse, write one row + lse
+    return {"n_chunks": n_chunks, "ms": round(times["chunked"], 4), "unchunked_with_lse_ms": round(times["whole"], 4),
+            "overhead": round(times["chunked"] / times["whole"] - 1.0, 4),
+            "tflops": round(fl / times["chunked"] / 1e9, 1), "merge_ms": round(times["merge"], 4),
+            "merge_gbs": round(merge_bytes / times["merge"] / 1e6, 1),
+            "merge_frac_hbm_peak": round(merge_bytes / times["merge"] / 1e6 / PEAK_HBM_GBS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -125,6 +174,7 @@ def main():
     ap.add_argument("--workload", default="1080p", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-sliced", action="store_true", help="skip timing the slicing schedule")
+    ap.add_argument("--no-chunked", action="store_true", help="skip timing chunked attention + merges")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -269,6 +319,10 @@ def main():
                          "bit_identical_to_unsliced": same}
         del x4, res
         torch.cuda.empty_cache()
+
+    if not args.no_chunked:
+        steps[0][1]()   # the spatial layer's q, k, v again (the timed steps end on the temporal layer)
+        out["chunked_attention"] = time_chunked_attention(lp, B, T, S, H, d, max(2, args.steps // 2), stream)
 
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_budget)

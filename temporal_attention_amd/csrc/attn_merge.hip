@@ -6,10 +6,14 @@
 // scaled scores; the union's output weights each part by exp(lse_part -
 // lse_union).
 //
-// One thread per (sequence, query, head) row: it reads both parts' log-sum-exps
-// and rows, then writes its own row and log-sum-exp, so the merge may run in
-// place on either input.  HBM-bound: 3 rows of d elements per row merged.
+// A group of LPR lanes of one wavefront handles a (sequence, query, head) row:
+// the lanes cover its 16-byte vectors, so a group reads one contiguous row.
+// A row never straddles wavefronts and every lane issues its reads of both
+// parts before any write, so the merge may run in place on either input.
+// HBM-bound: per row, two rows and two log-sum-exps in, one of each out.
 #include <math.h>
+
+#include <algorithm>
 
 #include "st_internal.h"
 
@@ -26,42 +30,46 @@ template <> struct Elem<float> {
   __device__ static float store(float x) { return x; }
 };
 
-template <typename T>
+template <typename T, int LPR>
 __global__ void __launch_bounds__(256) attn_merge_kernel(const T *oa, const float *la, const T *ob, const float *lb,
                                                          int64_t rows, int L, int H, int d, T *o, float *lse) {
-  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // row in [outer, L, H] order
-  if (r >= rows) return;
-  const int h = (int)(r % H);
-  const int64_t ql = r / H;                  // outer * L + query
-  const int qi = (int)(ql % L);
-  const int64_t seq = ql / L;
-  const int64_t li = (seq * H + h) * (int64_t)L + qi;
-  const float a = la[li], b = lb[li];
-  const float m = fmaxf(a, b);
-  const T *ra = oa + r * d, *rb = ob + r * d;
-  T *ro = o + r * d;
-  if (m == -INFINITY) {   // neither part has a valid key
-    for (int c = 0; c < d; ++c) ro[c] = Elem<T>::store(0.f);
-    lse[li] = -INFINITY;
-    return;
-  }
-  const float wa = expf(a - m), wb = expf(b - m);
-  const float tot = wa + wb;
-  const float fa = wa / tot, fb = wb / tot;
-  constexpr int VW = 16 / sizeof(T);   // elements per 16-byte vector
-  if (d % VW == 0) {                   // rows start 16-byte aligned (d * sizeof(T) a multiple of 16)
-    for (int c = 0; c < d; c += VW) {
-      const uint4 x = *reinterpret_cast<const uint4 *>(ra + c), y = *reinterpret_cast<const uint4 *>(rb + c);
-      const T *xe = reinterpret_cast<const T *>(&x), *ye = reinterpret_cast<const T *>(&y);
-      T z[VW];
+  constexpr int RPW = 64 / LPR;                 // rows per wavefront pass
+  constexpr int VW = 16 / sizeof(T);            // elements per 16-byte vector
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
+  const int j = lane % LPR;
+  const bool vec = d % VW == 0;                 // rows start 16-byte aligned
+  for (int64_t r0 = wave * RPW; r0 < rows; r0 += nwaves * RPW) {
+    const int64_t r = r0 + lane / LPR;          // row in [outer, L, H] order
+    if (r >= rows) continue;
+    const int h = (int)(r % H);
+    const int64_t ql = r / H;                   // outer * L + query
+    const int qi = (int)(ql % L);
+    const int64_t li = (ql / L * H + h) * (int64_t)L + qi;
+    const float a = la[li], b = lb[li];
+    const float m = fmaxf(a, b);
+    const bool empty = m == -INFINITY;          // neither part has a valid key
+    const float wa = empty ? 0.f : expf(a - m), wb = empty ? 0.f : expf(b - m);
+    const float tot = wa + wb;
+    const float fa = empty ? 0.f : wa / tot, fb = empty ? 0.f : wb / tot;
+    const T *ra = oa + r * d, *rb = ob + r * d;
+    T *ro = o + r * d;
+    if (vec) {
+      for (int c = j * VW; c < d; c += LPR * VW) {
+        const uint4 x = *reinterpret_cast<const uint4 *>(ra + c), y = *reinterpret_cast<const uint4 *>(rb + c);
+        const T *xe = reinterpret_cast<const T *>(&x), *ye = reinterpret_cast<const T *>(&y);
+        T z[VW];
 #pragma unroll
-      for (int j = 0; j < VW; ++j) z[j] = Elem<T>::store(fmaf(fa, Elem<T>::load(xe[j]), fb * Elem<T>::load(ye[j])));
-      *reinterpret_cast<uint4 *>(ro + c) = *reinterpret_cast<const uint4 *>(z);
+        for (int e = 0; e < VW; ++e)
+          z[e] = Elem<T>::store(fmaf(fa, Elem<T>::load(xe[e]), fb * Elem<T>::load(ye[e])));
+        *reinterpret_cast<uint4 *>(ro + c) = *reinterpret_cast<const uint4 *>(z);
+      }
+    } else {
+      for (int c = j; c < d; c += LPR) ro[c] = Elem<T>::store(fmaf(fa, Elem<T>::load(ra[c]), fb * Elem<T>::load(rb[c])));
     }
-  } else {
-    for (int c = 0; c < d; ++c) ro[c] = Elem<T>::store(fmaf(fa, Elem<T>::load(ra[c]), fb * Elem<T>::load(rb[c])));
+    if (j == 0) lse[li] = empty ? -INFINITY : m + logf(tot);
   }
-  lse[li] = m + logf(tot);
 }
 
 template <typename T>
@@ -73,20 +81,33 @@ __global__ void __launch_bounds__(256) attn_empty_kernel(T *o, float *lse, int64
 
 }  // namespace
 
+template <typename T, int LPR>
+void merge_launch(const void *o_a, const float *lse_a, const void *o_b, const float *lse_b, int64_t rows, int L, int H,
+                  int d, void *o, float *lse, hipStream_t s) {
+  const int64_t waves = (rows + 64 / LPR - 1) / (64 / LPR);
+  const uint32_t blocks = (uint32_t)std::min<int64_t>((waves + 3) / 4, 256 * 128);
+  hipLaunchKernelGGL((attn_merge_kernel<T, LPR>), dim3(blocks), dim3(256), 0, s, static_cast<const T *>(o_a), lse_a,
+                     static_cast<const T *>(o_b), lse_b, rows, L, H, d, static_cast<T *>(o), lse);
+}
+
 st_status launch_attn_merge(const void *o_a, const float *lse_a, const void *o_b, const float *lse_b, int64_t outer,
                             int L, int H, int d, int elem_bytes, void *o, float *lse, hipStream_t s) {
   const int64_t rows = outer * L * H;
   if (rows == 0) return ST_OK;
-  const int64_t blocks = (rows + 255) / 256;
-  if (blocks >= (1ll << 31)) return ST_EUNSUPPORTED;
-  if (elem_bytes == 2)
-    hipLaunchKernelGGL(attn_merge_kernel<u16>, dim3((uint32_t)blocks), dim3(256), 0, s,
-                       static_cast<const u16 *>(o_a), lse_a, static_cast<const u16 *>(o_b), lse_b, rows, L, H, d,
-                       static_cast<u16 *>(o), lse);
-  else
-    hipLaunchKernelGGL(attn_merge_kernel<float>, dim3((uint32_t)blocks), dim3(256), 0, s,
-                       static_cast<const float *>(o_a), lse_a, static_cast<const float *>(o_b), lse_b, rows, L, H,
-                       d, static_cast<float *>(o), lse);
+  // lanes per row: enough for the row's 16-byte vectors (or elements), a power of two
+  const int units = (d * elem_bytes) % 16 == 0 ? d * elem_bytes / 16 : d;
+  const int lpr = units <= 8 ? 8 : units <= 16 ? 16 : units <= 32 ? 32 : 64;
+  if (elem_bytes == 2) {
+    if (lpr == 8) merge_launch<u16, 8>(o_a, lse_a, o_b, lse_b, rows, L, H, d, o, lse, s);
+    else if (lpr == 16) merge_launch<u16, 16>(o_a, lse_a, o_b, lse_b, rows, L, H, d, o, lse, s);
+    else if (lpr == 32) merge_launch<u16, 32>(o_a, lse_a, o_b, lse_b, rows, L, H, d, o, lse, s);
+    else merge_launch<u16, 64>(o_a, lse_a, o_b, lse_b, rows, L, H, d, o, lse, s);
+  } else {
+    if (lpr == 8) merge_launch<float, 8>(o_a, lse_a, o_b, lse_b, rows, L, H, d, o, lse, s);
+    else if (lpr == 16) merge_launch<float, 16>(o_a, lse_a, o_b, lse_b, rows, L, H, d, o, lse, s);
+    else if (lpr == 32) merge_launch<float, 32>(o_a, lse_a, o_b, lse_b, rows, L, H, d, o, lse, s);
+    else merge_launch<float, 64>(o_a, lse_a, o_b, lse_b, rows, L, H, d, o, lse, s);
+  }
   return launch_status();
 }
 
