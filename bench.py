@@ -117,6 +117,70 @@ def cpu_baseline(inp, cfg, budget_s=20.0):
             "seconds": round(dt, 2), "host_cores_visible": len(os.sched_getaffinity(0))}
 
 
+def time_slicing(x, wsd, wtd, B, T, S, gw, C, H, d, stream, reps):
+    """The slicing schedule at one GPU: T padded with zero frames to a multiple of N_T, the
+    spatial layer per time slice and the temporal layer per space slice (t_valid = T), on one
+    stream (st_block_sliced) and with the slice gathers/scatters on a second stream
+    (st_block_sliced_2s).  Headline N_T = N_S = 4 (T 52) plus the sweep N_T, N_S in {1,2,4,8}."""
+    import torch
+
+    import st_synth
+    import temporal_attention_amd as st
+
+    sp = st.layer_weights(wsd["w_qkv"], wsd["w_o"], wsd["g_q"], wsd["g_k"])
+    tp = st.layer_weights(wtd["w_qkv"], wtd["w_o"], wtd["g_q"], wtd["g_k"])
+    side = torch.cuda.Stream()   # default priority
+    xv = x.view(B, T, S, C)
+    ref = {}
+
+    def run(nt, ns, two):
+        TT = -(-T // nt) * nt
+        xx = xv if TT == T else torch.cat([xv, torch.zeros_like(xv[:, :TT - T])], dim=1)
+        nb = st.st_block_sliced_workspace(B, TT, S, gw, C, H, d, nt, ns, st.ST_BF16)
+        ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        y = torch.empty((B, TT, S, C), dtype=torch.bfloat16, device="cuda")
+        if two:
+            fn = lambda: st.st_block_sliced_2s(xx, B, TT, T, S, gw, C, H, d, nt, ns, sp, tp, st_synth.EPS,  # noqa: E731
+                                               st_synth.ROPE_BASE, st.ST_BF16, y, ws, nb, side_stream=side)
+        else:
+            fn = lambda: st.st_block_sliced(xx, B, TT, T, S, gw, C, H, d, nt, ns, sp, tp, st_synth.EPS,  # noqa: E731
+                                            st_synth.ROPE_BASE, st.ST_BF16, y, ws, nb)
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        same = None
+        if (1, 1) in ref:
+            same = bool(torch.equal(y[:, :T], ref[(1, 1)]))
+        else:
+            ref[(1, 1)] = y[:, :T].clone()
+        del ws, y, xx
+        return TT, ms, same
+
+    sweep = {}
+    for nt in (1, 2, 4, 8):
+        for ns in (1, 2, 4, 8):
+            TT, ms1, same1 = run(nt, ns, False)
+            e = {"T": TT, "ms_one_stream": round(ms1, 4)}
+            if nt * ns > 1:
+                _, ms2, same2 = run(nt, ns, True)
+                e.update(ms_two_streams=round(ms2, 4), bit_identical=bool(same1 and same2))
+            sweep[f"{nt}x{ns}"] = e
+    base = sweep["1x1"]["ms_one_stream"]
+    head = sweep["4x4"]
+    sliced = {"n_t": 4, "n_s": 4, "T_padded": head["T"], "ms": head["ms_one_stream"],
+              "ms_two_streams": head["ms_two_streams"], "unsliced_native_ms": base,
+              "overhead": round(head["ms_one_stream"] / base - 1.0, 4),
+              "overhead_two_streams": round(head["ms_two_streams"] / base - 1.0, 4),
+              "bit_identical_to_unsliced": head["bit_identical"]}
+    return sliced, sweep
+
+
 def time_chunked_attention(lp, B, T, S, H, d, reps, stream, n_chunks=4):
     """Spatial attention of the step's q, k, v as a 4-way key split, the work of one GPU of a
     4-way ring: st_attn_chunk per key chunk (with log-sum-exp), folded together by three
@@ -290,34 +354,8 @@ def main():
     }
 
     if not args.no_sliced:
-        # the slicing schedule: T padded 51 -> 52 with a zero frame, N_T = N_S = 4
-        x4 = torch.cat([x.view(B, T, S, C), torch.zeros_like(x.view(B, T, S, C)[:, :1])], dim=1)
-        sp = st.layer_weights(wsd["w_qkv"], wsd["w_o"], wsd["g_q"], wsd["g_k"])
-        tp = st.layer_weights(wtd["w_qkv"], wtd["w_o"], wtd["g_q"], wtd["g_k"])
-        res = {}
-        for (nt, ns, TT, xx) in ((1, 1, T, x), (4, 4, T + 1, x4)):
-            nb = st.st_block_sliced_workspace(B, TT, S, gw, C, H, d, nt, ns, st.ST_BF16)
-            ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
-            y = torch.empty((B, TT, S, C), dtype=torch.bfloat16, device="cuda")
-            run = lambda: st.st_block_sliced(xx, B, TT, T, S, gw, C, H, d, nt, ns, sp, tp, st_synth.EPS,  # noqa: E731
-                                             st_synth.ROPE_BASE, st.ST_BF16, y, ws, nb)
-            run()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            reps = max(2, args.steps // 2)
-            e0.record(stream)
-            for _ in range(reps):
-                run()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            res[(nt, ns)] = (e0.elapsed_time(e1) / reps, y)
-            del ws
-        same = bool(torch.equal(res[(4, 4)][1][:, :T], res[(1, 1)][1]))
-        out["sliced"] = {"n_t": 4, "n_s": 4, "T_padded": T + 1, "ms": round(res[(4, 4)][0], 4),
-                         "unsliced_native_ms": round(res[(1, 1)][0], 4),
-                         "overhead": round(res[(4, 4)][0] / res[(1, 1)][0] - 1.0, 4),
-                         "bit_identical_to_unsliced": same}
-        del x4, res
+        out["sliced"], out["slicing_sweep"] = time_slicing(x, wsd, wtd, B, T, S, gw, C, H, d, stream,
+                                                           max(2, args.steps // 5))
         torch.cuda.empty_cache()
 
     if not args.no_chunked:

@@ -245,6 +245,31 @@ st_status st_block_sliced(const void *x, int B, int T, int t_valid, int S, int g
 size_t st_block_sliced_workspace(int B, int T, int S, int grid_w, int C, int H, int d,
                                  int n_t, int n_s, int dtype);
 
+/*
+ * st_block_sliced_2s -- st_block_sliced with the slicing schedule pipelined on
+ * two streams, the one-GPU form of the overlap the ScaleFusion review describes
+ * ("Core innovations", intra-layer scheduling: while one slice is computed, the
+ * next slice's data moves).  The layer computations (projections, attention)
+ * run on `stream`; the slice gathers, scatters and the two blocked rearranges
+ * run on `side_stream`, so slice i's gather overlaps slice i-1's computation
+ * and its scatter overlaps slice i+1's.  Slice buffers are double-buffered in
+ * the same workspace (st_block_sliced_workspace covers both variants).
+ *
+ *   stream, side_stream  two distinct, non-NULL hipStream_t (ST_EINVAL
+ *                        otherwise).  The call orders side_stream after the
+ *                        work already on stream, and stream after everything
+ *                        the call puts on side_stream: y is complete in
+ *                        stream order, exactly as for st_block_sliced.
+ * The result is bit-identical to st_block_sliced with the same arguments.  The
+ * call creates and releases HIP events (no device memory).  n_t = n_s = 1 runs
+ * entirely on `stream`.
+ */
+st_status st_block_sliced_2s(const void *x, int B, int T, int t_valid, int S, int grid_w, int C,
+                             int H, int d, int n_t, int n_s, const st_layer_weights *spatial,
+                             const st_layer_weights *temporal, float eps, float rope_base,
+                             int dtype, void *y, void *ws, size_t ws_bytes, void *stream,
+                             void *side_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,7 @@ ST_ROPE_NONE, ST_ROPE_1D, ST_ROPE_2D = 0, 1, 2
 EXPORTS = (
     "st_status_str", "st_rope_table_floats", "st_rope_table", "st_qkv_norm_rope", "st_out_proj",
     "st_attn_spatial", "st_attn_temporal", "st_attn_chunk", "st_attn_merge", "st_relayout", "st_block_sliced",
-    "st_block_sliced_workspace",
+    "st_block_sliced_2s", "st_block_sliced_workspace",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -67,6 +67,8 @@ _SIGS = {
     "st_block_sliced": (_i, [_p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, C.POINTER(st_layer_weights),
                              C.POINTER(st_layer_weights), _f, _f, _i, _p, _p, _sz, _p]),
     "st_block_sliced_workspace": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i, _i, _i]),
+    "st_block_sliced_2s": (_i, [_p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, C.POINTER(st_layer_weights),
+                                C.POINTER(st_layer_weights), _f, _f, _i, _p, _p, _sz, _p, _p]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -168,3 +170,19 @@ def st_block_sliced(x, B, T, t_valid, S, grid_w, C_, H, d, n_t, n_s, spatial, te
     tp = C.byref(temporal) if temporal is not None else None
     _check("st_block_sliced", lib.st_block_sliced(_ptr(x), B, T, t_valid, S, grid_w, C_, H, d, n_t, n_s, sp, tp, eps,
                                                   rope_base, dtype, _ptr(y), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def st_block_sliced_2s(x, B, T, t_valid, S, grid_w, C_, H, d, n_t, n_s, spatial, temporal, eps, rope_base, dtype, y,
+                       ws, ws_bytes, stream=None, side_stream=None):
+    """As st_block_sliced, with slice gathers/scatters on side_stream (a second, distinct stream)."""
+    sp = C.byref(spatial) if spatial is not None else None
+    tp = C.byref(temporal) if temporal is not None else None
+    _check("st_block_sliced_2s", lib.st_block_sliced_2s(_ptr(x), B, T, t_valid, S, grid_w, C_, H, d, n_t, n_s, sp, tp,
+                                                        eps, rope_base, dtype, _ptr(y), _ptr(ws), ws_bytes,
+                                                        _stream(stream), _side(side_stream)))
+
+
+def _side(s):
+    if s is None or isinstance(s, int):
+        return s
+    return s.cuda_stream

@@ -66,7 +66,7 @@ st_status do_attn(const void *q, const void *k, const void *v, int64_t outer, in
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 struct BlockPlan {
-  size_t rope2, rope1, xb, hb, xs, q, k, v, o, ys, total;
+  size_t rope2, rope1, xb, hb, xs, xs2, q, k, v, o, ys, ys2, total;
   int npos2, npos1;
 };
 
@@ -92,6 +92,7 @@ BlockPlan plan_block(int B, int T, int S, int grid_w, int C, int H, int d, int n
     p.hb = take(N * C * e);
     rows = std::max<int64_t>((int64_t)B * (T / n_t) * S, (int64_t)B * (S / n_s) * T);
     p.xs = take(rows * C * e);
+    p.xs2 = take(rows * C * e);   // slice buffers are double-buffered (two-stream pipeline)
   } else {
     p.hb = take(N * C * e);   // spatial output [B,T,S,C], later the temporal output [B,S,T,C]
     p.xs = take(N * C * e);   // [B,S,T,C] input of the temporal layer
@@ -102,6 +103,7 @@ BlockPlan plan_block(int B, int T, int S, int grid_w, int C, int H, int d, int n
   p.v = take(rows * hd * e);
   p.o = take(rows * hd * e);
   p.ys = sliced ? take(rows * C * e) : 0;
+  p.ys2 = sliced ? take(rows * C * e) : 0;
   p.total = off;
   return p;
 }
@@ -116,6 +118,192 @@ st_status run_layer(const void *x, int64_t outer, int L, int nv, int C, int H, i
   r = do_attn(q, k, v, outer, L, nv, H, d, (float)(1.0 / sqrt((double)d)), dt, o, temporal, s);
   if (r != ST_OK) return r;
   return do_linear(o, rows, H * d, w->w_o, C, dt, y, s);
+}
+
+// Events that order the two streams of the pipelined slicing schedule.  A
+// wait covers the work recorded most recently before the wait is enqueued.
+struct Events {
+  hipEvent_t ev[8] = {};
+  int n = 0;
+  st_status make(int count) {
+    for (n = 0; n < count; ++n)
+      if (hipEventCreateWithFlags(&ev[n], hipEventDisableTiming) != hipSuccess) return ST_ELAUNCH;
+    return ST_OK;
+  }
+  ~Events() {
+    for (int i = 0; i < n; ++i) hipEventDestroy(ev[i]);   // released once the pending work completes
+  }
+};
+
+// record on `from`, wait on `to` (no-op for one stream)
+st_status order(hipStream_t from, hipStream_t to, hipEvent_t e) {
+  if (from == to) return ST_OK;
+  if (hipEventRecord(e, from) != hipSuccess || hipStreamWaitEvent(to, e, 0) != hipSuccess) return ST_ELAUNCH;
+  return ST_OK;
+}
+
+// One layer phase of the slicing schedule over n slices.  gather(i, dst) and
+// scatter(i, src) run on `side`, layer(src, dst) on `main`; slice i's gather
+// overlaps layer i-1 and its scatter overlaps layer i+1.  xs[2], ys[2] are the
+// double-buffered slice inputs and outputs; ev holds 6 events: G[2], L[2], S[2].
+template <class Gather, class Layer, class Scatter>
+st_status slice_phase(int n, void *const xs[2], void *const ys[2], hipStream_t main, hipStream_t side, hipEvent_t *ev,
+                      Gather gather, Layer layer, Scatter scatter) {
+  hipEvent_t *G = ev, *Lv = ev + 2, *Sv = ev + 4;
+  const bool two = main != side;
+  st_status r = gather(0, xs[0]);
+  if (r != ST_OK) return r;
+  if (two && hipEventRecord(G[0], side) != hipSuccess) return ST_ELAUNCH;
+  for (int i = 0; i < n; ++i) {
+    const int b = i & 1, nb = b ^ 1;
+    if (i + 1 < n) {   // prefetch slice i+1; its buffer was read by layer i-1
+      if (two && i >= 1 && hipStreamWaitEvent(side, Lv[nb], 0) != hipSuccess) return ST_ELAUNCH;
+      r = gather(i + 1, xs[nb]);
+      if (r != ST_OK) return r;
+      if (two && hipEventRecord(G[nb], side) != hipSuccess) return ST_ELAUNCH;
+    }
+    if (two) {
+      if (hipStreamWaitEvent(main, G[b], 0) != hipSuccess) return ST_ELAUNCH;
+      if (i >= 2 && hipStreamWaitEvent(main, Sv[b], 0) != hipSuccess) return ST_ELAUNCH;   // ys[b] read by scatter i-2
+    }
+    r = layer(xs[b], ys[b]);
+    if (r != ST_OK) return r;
+    if (two && (hipEventRecord(Lv[b], main) != hipSuccess || hipStreamWaitEvent(side, Lv[b], 0) != hipSuccess))
+      return ST_ELAUNCH;
+    r = scatter(i, ys[b]);
+    if (r != ST_OK) return r;
+    if (two && hipEventRecord(Sv[b], side) != hipSuccess) return ST_ELAUNCH;
+  }
+  return ST_OK;
+}
+
+st_status block_sliced(const void *x, int B, int T, int t_valid, int S, int grid_w, int C, int H, int d, int n_t,
+                       int n_s, const st_layer_weights *spatial, const st_layer_weights *temporal, float eps,
+                       float rope_base, int dtype, void *y, void *ws, size_t ws_bytes, hipStream_t s,
+                       hipStream_t side) {
+  if (!dtype_ok(dtype)) return ST_EINVAL;
+  if (!x || !y || !spatial || !temporal) return ST_EINVAL;
+  for (const st_layer_weights *w : {spatial, temporal})
+    if (!w->w_qkv || !w->w_o || !w->g_q || !w->g_k) return ST_EINVAL;
+  if (B < 1 || T < 1 || S < 1 || C < 1 || H < 1 || grid_w < 1 || n_t < 1 || n_s < 1) return ST_EINVAL;
+  if (T % n_t || S % n_s || S % grid_w || t_valid < 1 || t_valid > T) return ST_EINVAL;
+  if (d < 4 || d % 4) return ST_EINVAL;
+  if (!(eps >= 0.f) || !isfinite(eps) || !(rope_base > 0.f) || !isfinite(rope_base)) return ST_EINVAL;
+  if (!head_dim_ok(d, dtype, ST_ROPE_2D)) return ST_EUNSUPPORTED;
+  if (dtype == ST_BF16 && (C % 64 || (H * d) % 64)) return ST_EUNSUPPORTED;
+  if (C % 4) return ST_EUNSUPPORTED;
+  if ((int64_t)B * T * S >= (1ll << 32) / 2) return ST_EUNSUPPORTED;
+  for (const st_layer_weights *w : {spatial, temporal})
+    for (const void *p : {w->w_qkv, w->w_o, (const void *)w->g_q, (const void *)w->g_k})
+      if (!aligned16(p)) return ST_EALIGN;
+  if (!aligned16(x) || !aligned16(y)) return ST_EALIGN;
+  const BlockPlan P = plan_block(B, T, S, grid_w, C, H, d, n_t, n_s, dtype);
+  if (!ws || ws_bytes < P.total) return ST_EWORKSPACE;
+  if (!aligned16(ws)) return ST_EALIGN;
+  const size_t e = esize(dtype);
+  const int64_t N = (int64_t)B * T * S;
+  const Range rx = rng(x, N * C * e), ry = rng(y, N * C * e), rw = rng(ws, (int64_t)P.total);
+  if (overlap(rx, ry) || overlap(ry, rw) || overlap(rx, rw)) return ST_EINVAL;
+
+  char *W = static_cast<char *>(ws);
+  float *rope2 = reinterpret_cast<float *>(W + P.rope2);
+  float *rope1 = reinterpret_cast<float *>(W + P.rope1);
+  void *q = W + P.q, *k = W + P.k, *v = W + P.v, *o = W + P.o;
+  st_status r = launch_rope_table(d, ST_ROPE_2D, rope_base, P.npos2, rope2, s);
+  if (r != ST_OK) return r;
+  r = launch_rope_table(d, ST_ROPE_1D, rope_base, P.npos1, rope1, s);
+  if (r != ST_OK) return r;
+  const RopeArgs r2{ST_ROPE_2D, P.npos2, rope2, S, 0, grid_w};   // rows [.., S]: h = s / W, w = s % W
+  const RopeArgs r1{ST_ROPE_1D, P.npos1, rope1, T, 0, 0};        // rows [.., T]: p = t
+  const int eb = (int)e;
+  const int64_t Cl = C;
+
+  if (n_t == 1 && n_s == 1) {
+    void *h = W + P.hb, *hs = W + P.xs;
+    r = run_layer(x, (int64_t)B * T, S, S, C, H, d, spatial, eps, r2, dtype, q, k, v, o, h, false, s);
+    if (r != ST_OK) return r;
+    {  // [B,T,S,C] -> [B,S,T,C]
+      const int64_t dims[4] = {B, T, S, C};
+      const int64_t ss[4] = {(int64_t)T * S * Cl, S * Cl, Cl, 1};
+      const int64_t ds[4] = {(int64_t)S * T * Cl, Cl, T * Cl, 1};
+      r = launch_relayout(h, ss, hs, ds, dims, 4, eb, s);
+      if (r != ST_OK) return r;
+    }
+    r = run_layer(hs, (int64_t)B * S, T, t_valid, C, H, d, temporal, eps, r1, dtype, q, k, v, o, h, true, s);
+    if (r != ST_OK) return r;
+    const int64_t dims[4] = {B, S, T, C};   // [B,S,T,C] -> [B,T,S,C]
+    const int64_t ss[4] = {(int64_t)S * T * Cl, T * Cl, Cl, 1};
+    const int64_t ds[4] = {(int64_t)T * S * Cl, Cl, S * Cl, 1};
+    return launch_relayout(h, ss, y, ds, dims, 4, eb, s);
+  }
+
+  // Sliced schedule.  Blocked layout xb[b][i][j][a][e][c] with a < T/N_T, e < S/N_S.
+  // Relayouts run on `side`, layers on `s`; with one stream this is the plain
+  // order of the pseudocode.
+  Events E;
+  if (side != s) {
+    r = E.make(8);
+    if (r != ST_OK) return r;
+    r = order(s, side, E.ev[6]);   // the side stream starts after the caller's earlier work
+    if (r != ST_OK) return r;
+  }
+  const int tt = T / n_t, ss_ = S / n_s;
+  const int64_t bstr[6] = {(int64_t)n_t * n_s * tt * ss_ * Cl, (int64_t)n_s * tt * ss_ * Cl, (int64_t)tt * ss_ * Cl,
+                           ss_ * Cl, Cl, 1};   // strides of [B, N_T, N_S, tt, ss, C]
+  void *xb = W + P.xb, *hb = W + P.hb;
+  void *const xs[2] = {W + P.xs, W + P.xs2}, *const ys[2] = {W + P.ys, W + P.ys2};
+  {  // step 2: x [B,T,S,C] viewed as [B, N_T, tt, N_S, ss, C] -> blocked
+    const int64_t dims[6] = {B, n_t, tt, n_s, ss_, C};
+    const int64_t sx[6] = {(int64_t)T * S * Cl, (int64_t)tt * S * Cl, S * Cl, ss_ * Cl, Cl, 1};
+    const int64_t db[6] = {bstr[0], bstr[1], bstr[3], bstr[2], bstr[4], 1};
+    r = launch_relayout(x, sx, xb, db, dims, 6, eb, side);
+    if (r != ST_OK) return r;
+  }
+  {  // spatial layer, one time slice at a time: gather [B, tt, S, C], compute, scatter back
+    const int64_t dims[5] = {B, tt, n_s, ss_, C};
+    const int64_t sb[5] = {bstr[0], bstr[3], bstr[2], bstr[4], 1};
+    const int64_t sc[5] = {(int64_t)tt * S * Cl, S * Cl, ss_ * Cl, Cl, 1};
+    r = slice_phase(
+        n_t, xs, ys, s, side, E.ev,
+        [&](int i, void *dst) {
+          return launch_relayout(static_cast<char *>(xb) + (int64_t)i * bstr[1] * eb, sb, dst, sc, dims, 5, eb, side);
+        },
+        [&](void *src, void *dst) {
+          return run_layer(src, (int64_t)B * tt, S, S, C, H, d, spatial, eps, r2, dtype, q, k, v, o, dst, false, s);
+        },
+        [&](int i, void *src) {
+          return launch_relayout(src, sc, static_cast<char *>(hb) + (int64_t)i * bstr[1] * eb, sb, dims, 5, eb, side);
+        });
+    if (r != ST_OK) return r;
+  }
+  void *yb = xb;   // temporal results go back into xb (its input was fully consumed by the spatial gathers)
+  {  // temporal layer, one space slice at a time: gather [B, ss, T, C], compute, scatter back
+    const int64_t dims[5] = {B, n_t, tt, ss_, C};
+    const int64_t sb[5] = {bstr[0], bstr[1], bstr[3], bstr[4], 1};
+    const int64_t sc[5] = {(int64_t)ss_ * T * Cl, (int64_t)tt * Cl, Cl, (int64_t)T * Cl, 1};
+    r = slice_phase(
+        n_s, xs, ys, s, side, E.ev,
+        [&](int j, void *dst) {
+          return launch_relayout(static_cast<const char *>(hb) + (int64_t)j * bstr[2] * eb, sb, dst, sc, dims, 5, eb,
+                                 side);
+        },
+        [&](void *src, void *dst) {
+          return run_layer(src, (int64_t)B * ss_, T, t_valid, C, H, d, temporal, eps, r1, dtype, q, k, v, o, dst, true,
+                           s);
+        },
+        [&](int j, void *src) {
+          return launch_relayout(src, sc, static_cast<char *>(yb) + (int64_t)j * bstr[2] * eb, sb, dims, 5, eb, side);
+        });
+    if (r != ST_OK) return r;
+  }
+  {  // step 10: blocked -> [B, T, S, C]
+    const int64_t dims[6] = {B, n_t, tt, n_s, ss_, C};
+    const int64_t sx[6] = {(int64_t)T * S * Cl, (int64_t)tt * S * Cl, S * Cl, ss_ * Cl, Cl, 1};
+    const int64_t db[6] = {bstr[0], bstr[1], bstr[3], bstr[2], bstr[4], 1};
+    r = launch_relayout(yb, db, y, sx, dims, 6, eb, side);
+    if (r != ST_OK) return r;
+  }
+  return order(side, s, E.ev[7]);   // the caller's stream sees the finished output
 }
 
 }  // namespace
@@ -298,110 +486,17 @@ size_t st_block_sliced_workspace(int B, int T, int S, int grid_w, int C, int H, 
 st_status st_block_sliced(const void *x, int B, int T, int t_valid, int S, int grid_w, int C, int H, int d, int n_t,
                           int n_s, const st_layer_weights *spatial, const st_layer_weights *temporal, float eps,
                           float rope_base, int dtype, void *y, void *ws, size_t ws_bytes, void *stream) {
-  if (!dtype_ok(dtype)) return ST_EINVAL;
-  if (!x || !y || !spatial || !temporal) return ST_EINVAL;
-  for (const st_layer_weights *w : {spatial, temporal})
-    if (!w->w_qkv || !w->w_o || !w->g_q || !w->g_k) return ST_EINVAL;
-  if (B < 1 || T < 1 || S < 1 || C < 1 || H < 1 || grid_w < 1 || n_t < 1 || n_s < 1) return ST_EINVAL;
-  if (T % n_t || S % n_s || S % grid_w || t_valid < 1 || t_valid > T) return ST_EINVAL;
-  if (d < 4 || d % 4) return ST_EINVAL;
-  if (!(eps >= 0.f) || !isfinite(eps) || !(rope_base > 0.f) || !isfinite(rope_base)) return ST_EINVAL;
-  if (!head_dim_ok(d, dtype, ST_ROPE_2D)) return ST_EUNSUPPORTED;
-  if (dtype == ST_BF16 && (C % 64 || (H * d) % 64)) return ST_EUNSUPPORTED;
-  if (C % 4) return ST_EUNSUPPORTED;
-  if ((int64_t)B * T * S >= (1ll << 32) / 2) return ST_EUNSUPPORTED;
-  for (const st_layer_weights *w : {spatial, temporal})
-    for (const void *p : {w->w_qkv, w->w_o, (const void *)w->g_q, (const void *)w->g_k})
-      if (!aligned16(p)) return ST_EALIGN;
-  if (!aligned16(x) || !aligned16(y)) return ST_EALIGN;
-  const BlockPlan P = plan_block(B, T, S, grid_w, C, H, d, n_t, n_s, dtype);
-  if (!ws || ws_bytes < P.total) return ST_EWORKSPACE;
-  if (!aligned16(ws)) return ST_EALIGN;
-  const size_t e = esize(dtype);
-  const int64_t N = (int64_t)B * T * S;
-  const Range rx = rng(x, N * C * e), ry = rng(y, N * C * e), rw = rng(ws, (int64_t)P.total);
-  if (overlap(rx, ry) || overlap(ry, rw) || overlap(rx, rw)) return ST_EINVAL;
+  return block_sliced(x, B, T, t_valid, S, grid_w, C, H, d, n_t, n_s, spatial, temporal, eps, rope_base, dtype, y, ws,
+                      ws_bytes, (hipStream_t)stream, (hipStream_t)stream);
+}
 
-  hipStream_t s = (hipStream_t)stream;
-  char *W = static_cast<char *>(ws);
-  float *rope2 = reinterpret_cast<float *>(W + P.rope2);
-  float *rope1 = reinterpret_cast<float *>(W + P.rope1);
-  void *q = W + P.q, *k = W + P.k, *v = W + P.v, *o = W + P.o;
-  st_status r = launch_rope_table(d, ST_ROPE_2D, rope_base, P.npos2, rope2, s);
-  if (r != ST_OK) return r;
-  r = launch_rope_table(d, ST_ROPE_1D, rope_base, P.npos1, rope1, s);
-  if (r != ST_OK) return r;
-  const RopeArgs r2{ST_ROPE_2D, P.npos2, rope2, S, 0, grid_w};   // rows [.., S]: h = s / W, w = s % W
-  const RopeArgs r1{ST_ROPE_1D, P.npos1, rope1, T, 0, 0};        // rows [.., T]: p = t
-  const int eb = (int)e;
-  const int64_t Cl = C;
-
-  if (n_t == 1 && n_s == 1) {
-    void *h = W + P.hb, *hs = W + P.xs;
-    r = run_layer(x, (int64_t)B * T, S, S, C, H, d, spatial, eps, r2, dtype, q, k, v, o, h, false, s);
-    if (r != ST_OK) return r;
-    {  // [B,T,S,C] -> [B,S,T,C]
-      const int64_t dims[4] = {B, T, S, C};
-      const int64_t ss[4] = {(int64_t)T * S * Cl, S * Cl, Cl, 1};
-      const int64_t ds[4] = {(int64_t)S * T * Cl, Cl, T * Cl, 1};
-      r = launch_relayout(h, ss, hs, ds, dims, 4, eb, s);
-      if (r != ST_OK) return r;
-    }
-    r = run_layer(hs, (int64_t)B * S, T, t_valid, C, H, d, temporal, eps, r1, dtype, q, k, v, o, h, true, s);
-    if (r != ST_OK) return r;
-    const int64_t dims[4] = {B, S, T, C};   // [B,S,T,C] -> [B,T,S,C]
-    const int64_t ss[4] = {(int64_t)S * T * Cl, T * Cl, Cl, 1};
-    const int64_t ds[4] = {(int64_t)T * S * Cl, Cl, S * Cl, 1};
-    return launch_relayout(h, ss, y, ds, dims, 4, eb, s);
-  }
-
-  // Sliced schedule.  Blocked layout xb[b][i][j][a][e][c] with a < T/N_T, e < S/N_S.
-  const int tt = T / n_t, ss_ = S / n_s;
-  const int64_t bstr[6] = {(int64_t)n_t * n_s * tt * ss_ * Cl, (int64_t)n_s * tt * ss_ * Cl, (int64_t)tt * ss_ * Cl,
-                           ss_ * Cl, Cl, 1};   // strides of [B, N_T, N_S, tt, ss, C]
-  void *xb = W + P.xb, *hb = W + P.hb, *xs = W + P.xs, *ys = W + P.ys;
-  {  // step 2: x [B,T,S,C] viewed as [B, N_T, tt, N_S, ss, C] -> blocked
-    const int64_t dims[6] = {B, n_t, tt, n_s, ss_, C};
-    const int64_t sx[6] = {(int64_t)T * S * Cl, (int64_t)tt * S * Cl, S * Cl, ss_ * Cl, Cl, 1};
-    const int64_t db[6] = {bstr[0], bstr[1], bstr[3], bstr[2], bstr[4], 1};
-    r = launch_relayout(x, sx, xb, db, dims, 6, eb, s);
-    if (r != ST_OK) return r;
-  }
-  // spatial layer, one time slice at a time: gather [B, tt, S, C], compute, scatter back
-  for (int i = 0; i < n_t; ++i) {
-    const int64_t dims[5] = {B, tt, n_s, ss_, C};
-    const int64_t sb[5] = {bstr[0], bstr[3], bstr[2], bstr[4], 1};
-    const int64_t sc[5] = {(int64_t)tt * S * Cl, S * Cl, ss_ * Cl, Cl, 1};
-    char *blk = static_cast<char *>(xb) + (int64_t)i * bstr[1] * eb;
-    r = launch_relayout(blk, sb, xs, sc, dims, 5, eb, s);
-    if (r != ST_OK) return r;
-    r = run_layer(xs, (int64_t)B * tt, S, S, C, H, d, spatial, eps, r2, dtype, q, k, v, o, ys, false, s);
-    if (r != ST_OK) return r;
-    char *hblk = static_cast<char *>(hb) + (int64_t)i * bstr[1] * eb;
-    r = launch_relayout(ys, sc, hblk, sb, dims, 5, eb, s);
-    if (r != ST_OK) return r;
-  }
-  // temporal layer, one space slice at a time: gather [B, ss, T, C], compute, scatter back into xb (reused as yb)
-  void *yb = xb;
-  for (int j = 0; j < n_s; ++j) {
-    const int64_t dims[5] = {B, n_t, tt, ss_, C};
-    const int64_t sb[5] = {bstr[0], bstr[1], bstr[3], bstr[4], 1};
-    const int64_t sc[5] = {(int64_t)ss_ * T * Cl, (int64_t)tt * Cl, Cl, (int64_t)T * Cl, 1};
-    const char *hblk = static_cast<const char *>(hb) + (int64_t)j * bstr[2] * eb;
-    r = launch_relayout(hblk, sb, xs, sc, dims, 5, eb, s);
-    if (r != ST_OK) return r;
-    r = run_layer(xs, (int64_t)B * ss_, T, t_valid, C, H, d, temporal, eps, r1, dtype, q, k, v, o, ys, true, s);
-    if (r != ST_OK) return r;
-    char *yblk = static_cast<char *>(yb) + (int64_t)j * bstr[2] * eb;
-    r = launch_relayout(ys, sc, yblk, sb, dims, 5, eb, s);
-    if (r != ST_OK) return r;
-  }
-  {  // step 10: blocked -> [B, T, S, C]
-    const int64_t dims[6] = {B, n_t, tt, n_s, ss_, C};
-    const int64_t sx[6] = {(int64_t)T * S * Cl, (int64_t)tt * S * Cl, S * Cl, ss_ * Cl, Cl, 1};
-    const int64_t db[6] = {bstr[0], bstr[1], bstr[3], bstr[2], bstr[4], 1};
-    return launch_relayout(yb, db, y, sx, dims, 6, eb, s);
-  }
+st_status st_block_sliced_2s(const void *x, int B, int T, int t_valid, int S, int grid_w, int C, int H, int d, int n_t,
+                             int n_s, const st_layer_weights *spatial, const st_layer_weights *temporal, float eps,
+                             float rope_base, int dtype, void *y, void *ws, size_t ws_bytes, void *stream,
+                             void *side_stream) {
+  if (!side_stream || side_stream == stream) return ST_EINVAL;
+  return block_sliced(x, B, T, t_valid, S, grid_w, C, H, d, n_t, n_s, spatial, temporal, eps, rope_base, dtype, y, ws,
+                      ws_bytes, (hipStream_t)stream, (hipStream_t)side_stream);
 }
 
 }  // extern "C"

@@ -197,6 +197,13 @@ def test_block_workspace_and_validation():
         a.update(kw)
         return code(st.st_block_sliced, *a.values())
     assert c(T=51) == st.ST_EINVAL                 # T % n_t
+    a2 = list(base.values())
+    with pytest.raises(st.STError) as e:           # the side stream must be a second, distinct stream
+        st.st_block_sliced_2s(*a2, stream=0x1234, side_stream=0x1234)
+    assert e.value.code == st.ST_EINVAL
+    with pytest.raises(st.STError) as e:
+        st.st_block_sliced_2s(*a2, stream=0x1234, side_stream=None)
+    assert e.value.code == st.ST_EINVAL
     assert c(t_valid=0) == st.ST_EINVAL
     assert c(grid_w=121) == st.ST_EINVAL           # S % grid_w
     assert c(spatial=None) == st.ST_EINVAL

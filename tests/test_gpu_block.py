@@ -46,13 +46,18 @@ def host_weights(w):
                 g_k=w["g_k"].astype(np.float64))
 
 
-def run_block(xd, wd, T, t_valid, S, grid_w, C, H, d, n_t, n_s, dt):
+def run_block(xd, wd, T, t_valid, S, grid_w, C, H, d, n_t, n_s, dt, two_streams=False):
     sp = st.layer_weights(wd["s"]["w_qkv"], wd["s"]["w_o"], wd["s"]["g_q"], wd["s"]["g_k"])
     tp = st.layer_weights(wd["t"]["w_qkv"], wd["t"]["w_o"], wd["t"]["g_q"], wd["t"]["g_k"])
     nbytes = st.st_block_sliced_workspace(1, T, S, grid_w, C, H, d, n_t, n_s, dt)
     ws = t_.empty(nbytes, dtype=t_.uint8, device="cuda")
     y = empty((1, T, S, C), dt == st.ST_BF16)
-    st.st_block_sliced(xd, 1, T, t_valid, S, grid_w, C, H, d, n_t, n_s, sp, tp, EPS, BASE, dt, y, ws, nbytes)
+    if two_streams:   # slice gathers/scatters on a second stream (default priority)
+        side = t_.cuda.Stream()
+        st.st_block_sliced_2s(xd, 1, T, t_valid, S, grid_w, C, H, d, n_t, n_s, sp, tp, EPS, BASE, dt, y, ws, nbytes,
+                              side_stream=side)
+    else:
+        st.st_block_sliced(xd, 1, T, t_valid, S, grid_w, C, H, d, n_t, n_s, sp, tp, EPS, BASE, dt, y, ws, nbytes)
     t_.cuda.synchronize()
     return y
 
@@ -140,6 +145,8 @@ def test_sliced_equals_unsliced_bf16(n_t, n_s):
     y1 = run_block(xd, wd, T, T, S, grid_w, C, H, d, 1, 1, st.ST_BF16)
     ys = run_block(xd, wd, T, T, S, grid_w, C, H, d, n_t, n_s, st.ST_BF16)
     assert t_.equal(y1, ys)
+    y2 = run_block(xd, wd, T, T, S, grid_w, C, H, d, n_t, n_s, st.ST_BF16, two_streams=True)
+    assert t_.equal(y1, y2)
 
 
 def test_padded_masked_schedule_equals_unpadded():
@@ -150,6 +157,8 @@ def test_padded_masked_schedule_equals_unpadded():
     y1 = run_block(to_dev(x), wd, T, T, S, grid_w, C, H, d, 1, 1, st.ST_BF16)
     yp = run_block(to_dev(xp), wd, T + 1, T, S, grid_w, C, H, d, 2, 4, st.ST_BF16)
     assert t_.equal(yp[:, :T], y1)
+    y2 = run_block(to_dev(xp), wd, T + 1, T, S, grid_w, C, H, d, 2, 4, st.ST_BF16, two_streams=True)
+    assert t_.equal(y2, yp)
     wh = {k: host_weights(v) for k, v in w.items()}
     y_ref = oracle.block_sliced(f64(xp), wh["s"], wh["t"], H, d, grid_w, EPS, BASE, 2, 4, t_valid=T)
     assert_close(f64(yp)[:, :T], y_ref[:, :T], True, "padded block")
@@ -211,6 +220,8 @@ def test_1080p_full_size_sampled_and_sliced_schedule():
     x4 = t_.cat([xd, t_.zeros_like(xd[:, :1])], dim=1)
     y4 = run_block(x4, wd, T + 1, T, S, grid_w, C, H, d, 4, 4, st.ST_BF16)
     assert t_.equal(y4[:, :T], y3)
+    y4s = run_block(x4, wd, T + 1, T, S, grid_w, C, H, d, 4, 4, st.ST_BF16, two_streams=True)
+    assert t_.equal(y4s, y4)
 
 
 def test_4096px_image_attention_sampled():
