@@ -257,6 +257,38 @@ def from_blocked(xb: np.ndarray) -> np.ndarray:
 # --------------------------------------------------------------------------- #
 # Layers and the block                                                         #
 # --------------------------------------------------------------------------- #
+# --------------------------------------------------------------------------- #
+# The all-to-all between the two shardings ([SF] layer table, execution flow)  #
+# --------------------------------------------------------------------------- #
+def shard(x: np.ndarray, P: int, axis: int) -> list:
+    """x [B, T, S, C] split into P equal blocks along axis 1 (frames) or 2 (patches); block r is rank r's."""
+    n = x.shape[axis] // P
+    return [np.take(x, np.arange(r * n, (r + 1) * n), axis=axis) for r in range(P)]
+
+
+def all_to_all(send: list) -> list:
+    """send[r][q] is the block rank r sends to rank q; rank q receives recv[q][r] = send[r][q]."""
+    P = len(send)
+    return [[send[r][q] for r in range(P)] for q in range(P)]
+
+
+def a2a_s_to_t(shards_s: list) -> list:
+    """Patch-sharded [B, T, S/P, C] per rank -> frame-sharded [B, T/P, S, C] per rank (P = 1: identity).
+
+    Rank r sends frame block q of its patches to rank q; rank q lays the received patch blocks
+    side by side, in rank order, along S."""
+    P = len(shards_s)
+    recv = all_to_all([shard(xs, P, 1) for xs in shards_s])
+    return [np.concatenate(recv[q], axis=2) for q in range(P)]
+
+
+def a2a_t_to_s(shards_t: list) -> list:
+    """Frame-sharded [B, T/P, S, C] per rank -> patch-sharded [B, T, S/P, C] per rank: the inverse exchange."""
+    P = len(shards_t)
+    recv = all_to_all([shard(xt, P, 2) for xt in shards_t])
+    return [np.concatenate(recv[q], axis=1) for q in range(P)]
+
+
 def spatial_layer(x, wts: dict, H: int, d: int, grid_w: int, eps: float, base: float):
     """Spatial layer on x [B, T, S, C]: attention over the S patches of each frame."""
     B, T, S, C = x.shape

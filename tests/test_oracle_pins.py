@@ -471,6 +471,32 @@ def test_chunk_wrappers_are_per_sequence_with_head_major_lse():
 
 
 # --------------------------------------------------------------------------- #
+# All-to-all between the patch-sharded and frame-sharded layouts              #
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("B,T,S,C,P", [(1, 4, 6, 3, 2), (2, 6, 6, 2, 3), (1, 8, 4, 5, 4), (2, 3, 5, 2, 1)])
+def test_a2a_redistributes_by_index(B, T, S, C, P):
+    x = rng(90 + P).standard_normal((B, T, S, C))
+    tp, sp = T // P, S // P
+    out = oracle.a2a_s_to_t([x[:, :, r * sp:(r + 1) * sp] for r in range(P)])
+    for q in range(P):                                 # rank q: frames q*T/P .. of every patch
+        assert out[q].shape == (B, tp, S, C)
+        for b in range(B):
+            for t in range(tp):
+                for s in range(S):
+                    for c in range(C):
+                        assert out[q][b, t, s, c] == x[b, q * tp + t, s, c]
+    back = oracle.a2a_t_to_s(out)
+    for r in range(P):
+        assert np.array_equal(back[r], x[:, :, r * sp:(r + 1) * sp])
+
+
+def test_all_to_all_is_a_block_transpose():
+    send = [[(r, q) for q in range(3)] for r in range(3)]
+    recv = oracle.all_to_all(send)
+    assert all(recv[q][r] == (r, q) for r in range(3) for q in range(3))
+
+
+# --------------------------------------------------------------------------- #
 # Planted mistakes: each must be caught by a pin above                         #
 # --------------------------------------------------------------------------- #
 def test_pins_catch_rope_sign_error():
