@@ -181,6 +181,39 @@ def time_slicing(x, wsd, wtd, B, T, S, gw, C, H, d, stream, reps):
     return sliced, sweep
 
 
+def time_a2a_local(B, T, S, C, P, reps, stream):
+    """One rank's local pack and unpack around the P-way all-to-all at the 1080p per-GPU shape
+    (T padded to a multiple of P): each moves one rank's share, B*T*S*C/P elements, once."""
+    import torch
+
+    from temporal_attention_amd import a2a
+
+    TT = -(-T // P) * P
+    tp, sp = TT // P, S // P
+    xs = torch.empty((B, TT, sp, C), dtype=torch.bfloat16, device="cuda")   # contents irrelevant to a copy
+    xt = torch.empty((B, tp, S, C), dtype=torch.bfloat16, device="cuda")
+    buf = torch.empty((P, B, tp, sp, C), dtype=torch.bfloat16, device="cuda")
+    ops = {"pack_s2t": lambda: a2a.pack_s2t(xs, buf, B, TT, sp, C, P),
+           "unpack_s2t": lambda: a2a.unpack_s2t(buf, xt, B, TT, sp, C, P),
+           "pack_t2s": lambda: a2a.pack_t2s(xt, buf, B, TT, S, C, P),
+           "unpack_t2s": lambda: a2a.unpack_t2s(buf, xs, B, TT, S, C, P)}
+    nbytes = 2.0 * xs.numel() * 2
+    res = {"P": P, "T_padded": TT, "rank_shape": [B, TT, sp, C], "bytes_moved_per_op": int(nbytes),
+           "note": "one rank's share (0.13 GB) fits the 256 MB Infinity Cache, so rates can exceed HBM's"}
+    for name, fn in ops.items():
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        res[name] = {"ms": round(ms, 4), "gbs": round(nbytes / ms / 1e6, 1)}
+    return res
+
+
 def time_chunked_attention(lp, B, T, S, H, d, reps, stream, n_chunks=4):
     """Spatial attention of the step's q, k, v as a 4-way key split, the work of one GPU of a
     4-way ring: st_attn_chunk per key chunk (with log-sum-exp), folded together by three
@@ -239,6 +272,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-sliced", action="store_true", help="skip timing the slicing schedule")
     ap.add_argument("--no-chunked", action="store_true", help="skip timing chunked attention + merges")
+    ap.add_argument("--no-a2a", action="store_true", help="skip timing the all-to-all pack/unpack")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -361,6 +395,9 @@ def main():
     if not args.no_chunked:
         steps[0][1]()   # the spatial layer's q, k, v again (the timed steps end on the temporal layer)
         out["chunked_attention"] = time_chunked_attention(lp, B, T, S, H, d, max(2, args.steps // 2), stream)
+
+    if not args.no_a2a:
+        out["a2a_local"] = time_a2a_local(B, T, S, C, 8, max(3, args.steps), stream)
 
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_budget)

@@ -105,3 +105,15 @@ def to_f64(a: np.ndarray) -> np.ndarray:
     if a.dtype == np.uint16:
         return bf16_bits_to_f32(a).astype(np.float64)
     return np.asarray(a, dtype=np.float64)
+
+
+def bits(shape, seed: int, dtype: str = "bf16") -> np.ndarray:
+    """Uniformly random storage words (uint16 for bf16, uint32 reinterpreted as float32 for f32), seeded.
+
+    For pure data movement (relayouts, exchanges): every bit pattern is as good as any other, and
+    distinct words make a misplaced element visible.  Float32 words avoid the NaN range."""
+    r = np.random.default_rng(seed)
+    if dtype == "bf16":
+        return r.integers(0, 1 << 16, size=shape, dtype=np.uint16)
+    return r.integers(0, 0x7F000000, size=shape, dtype=np.uint32).view(np.float32)
+
