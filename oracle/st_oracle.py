@@ -20,6 +20,10 @@ Sources (page titles as printed on the pages):
   [PF]  PipeFusion technical summary, "Problem definition": attention cost is
         quadratic in sequence length; sequence parallelism (DeepSpeed-Ulysses,
         Ring-Attention) splits the sequence across devices.
+  [VM]  CoCoDiff page, section "V-Major selective communication": per denoising
+        step, each V vector is compared with the previous step's by L1
+        distance; only vectors whose change exceeds a threshold are active
+        (their Q, K, V are communicated), the rest come from the cache.
   [SW]  "Technical Summary: SwiftFusion", sections "Topology-Aware Communication
         Scheduling" (Ring Attention inside a machine) and "Torus Attention"
         (attention computed chunk by chunk as the chunks arrive).
@@ -41,6 +45,10 @@ Readings where the pages are silent (each is also listed in the design notes):
       each chunk yields its normalised output and the log-sum-exp of its
       scaled scores (natural log; -inf for a chunk with no valid key), and two
       disjoint chunks combine with weights exp(lse_chunk - lse_union).
+  R6  V-Major ([VM]): a "vector" is one (token, head) row of V (d values); its
+      distance is sum_j |v_new_j - v_cache_j|; it is active when the distance
+      is strictly greater than the caller's threshold (the page gives no
+      value); active rows are the ones whose V replaces the cached V.
 """
 from __future__ import annotations
 
@@ -287,6 +295,19 @@ def a2a_t_to_s(shards_t: list) -> list:
     P = len(shards_t)
     recv = all_to_all([shard(xt, P, 2) for xt in shards_t])
     return [np.concatenate(recv[q], axis=1) for q in range(P)]
+
+
+# --------------------------------------------------------------------------- #
+# V-Major change detection ([VM], R6)                                          #
+# --------------------------------------------------------------------------- #
+def v_change(v_new, v_cache, threshold: float):
+    """v_new, v_cache [rows, H, d] -> (dist [rows, H], active mask [rows, H], active flat
+    indices r*H + h in increasing order, refreshed cache: v_new where active, else v_cache)."""
+    a, b = np.asarray(v_new, np.float64), np.asarray(v_cache, np.float64)
+    dist = np.sum(np.abs(a - b), axis=-1)
+    mask = dist > threshold
+    cache = np.where(mask[..., None], a, b)
+    return dist, mask, np.flatnonzero(mask), cache
 
 
 def spatial_layer(x, wts: dict, H: int, d: int, grid_w: int, eps: float, base: float):

@@ -497,6 +497,31 @@ def test_all_to_all_is_a_block_transpose():
 
 
 # --------------------------------------------------------------------------- #
+# V-Major change detection (R6)                                               #
+# --------------------------------------------------------------------------- #
+def test_v_change_by_loops_and_special_cases():
+    r = rng(95)
+    rows, H, d = 5, 3, 4
+    vn, vc = r.standard_normal((rows, H, d)), r.standard_normal((rows, H, d))
+    vc[1, 2] = vn[1, 2]                                      # unchanged vector
+    vc[3, 0] = vn[3, 0] + np.array([0.5, -0.25, 0.0, 0.25])  # distance exactly 1.0
+    dist, mask, idx, cache = oracle.v_change(vn, vc, 1.0)
+    for i in range(rows):
+        for h in range(H):
+            want = math.fsum(abs(float(vn[i, h, j]) - float(vc[i, h, j])) for j in range(d))
+            assert dist[i, h] == pytest.approx(want, rel=1e-15, abs=0)
+            assert mask[i, h] == (want > 1.0)
+            assert np.array_equal(cache[i, h], vn[i, h] if want > 1.0 else vc[i, h])
+    assert dist[1, 2] == 0.0 and not mask[1, 2]
+    assert dist[3, 0] == 1.0 and not mask[3, 0]               # strictly greater than the threshold
+    assert list(idx) == [i * H + h for i in range(rows) for h in range(H) if mask[i, h]]
+    _, m0, _, c0 = oracle.v_change(vn, vc, 0.0)                 # threshold 0: every changed vector
+    assert m0.sum() == rows * H - 1 and np.array_equal(c0, vn)
+    _, mi, ii, ci = oracle.v_change(vn, vc, math.inf)          # infinite threshold: nothing moves
+    assert not mi.any() and ii.size == 0 and np.array_equal(ci, vc)
+
+
+# --------------------------------------------------------------------------- #
 # Planted mistakes: each must be caught by a pin above                         #
 # --------------------------------------------------------------------------- #
 def test_pins_catch_rope_sign_error():
