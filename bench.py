@@ -181,6 +181,43 @@ def time_slicing(x, wsd, wtd, B, T, S, gw, C, H, d, stream, reps):
     return sliced, sweep
 
 
+def time_v_change(lp, reps, stream):
+    """V-Major change detection over the step's V ([N, H, d]) against a cache that differs on every
+    fifth token (so ~20% of vectors are active at threshold 1.0), without refreshing the cache so
+    every repetition sees the same input; one more call with the refresh."""
+    import torch
+
+    import temporal_attention_amd as st
+
+    N, H, d = lp.N, lp.H, lp.d
+    v = lp.v
+    cache = v.clone()
+    cache.view(N, H, d)[::5] += 1.0
+    mask = torch.empty((N, H), dtype=torch.uint8, device="cuda")
+    idx = torch.empty(N * H, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(1, dtype=torch.int64, device="cuda")
+    run = lambda upd: st.st_v_change(v, cache, N, H, d, 1.0, st.ST_BF16, mask, idx, cnt, upd)  # noqa: E731
+    run(0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        run(0)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    n_act = int(cnt.item())
+    nbytes = 2.0 * N * H * d * 2 + N * H + 4.0 * n_act      # read both V, write mask and indices
+    e0.record(stream)
+    run(1)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_upd = e0.elapsed_time(e1)
+    return {"vectors": N * H, "active": n_act, "threshold": 1.0, "ms": round(ms, 4),
+            "gbs": round(nbytes / ms / 1e6, 1), "frac_hbm_peak": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4),
+            "ms_with_cache_refresh": round(ms_upd, 4)}
+
+
 def time_a2a_local(B, T, S, C, P, reps, stream):
     """One rank's local pack and unpack around the P-way all-to-all at the 1080p per-GPU shape
     (T padded to a multiple of P): each moves one rank's share, B*T*S*C/P elements, once."""
@@ -273,6 +310,7 @@ def main():
     ap.add_argument("--no-sliced", action="store_true", help="skip timing the slicing schedule")
     ap.add_argument("--no-chunked", action="store_true", help="skip timing chunked attention + merges")
     ap.add_argument("--no-a2a", action="store_true", help="skip timing the all-to-all pack/unpack")
+    ap.add_argument("--no-vchange", action="store_true", help="skip timing the V-Major change detection")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -395,6 +433,9 @@ def main():
     if not args.no_chunked:
         steps[0][1]()   # the spatial layer's q, k, v again (the timed steps end on the temporal layer)
         out["chunked_attention"] = time_chunked_attention(lp, B, T, S, H, d, max(2, args.steps // 2), stream)
+
+    if not args.no_vchange:
+        out["v_change"] = time_v_change(lp, max(3, args.steps), stream)
 
     if not args.no_a2a:
         out["a2a_local"] = time_a2a_local(B, T, S, C, 8, max(3, args.steps), stream)

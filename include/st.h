@@ -193,6 +193,31 @@ st_status st_attn_merge(const void *o_a, const float *lse_a, const void *o_b, co
                         int H, int d, int dtype, void *out, float *lse, void *stream);
 
 /*
+ * st_v_change -- V-Major change detection (CoCoDiff page, "V-Major selective
+ * communication"): per denoising step, a V vector whose L1 change against the
+ * cached vector of the previous step exceeds a threshold is active (its Q, K,
+ * V are communicated); the others are read from the cache.  A vector is one
+ * (token, head) row of V:
+ *   dist[v] = sum_j |v_new[v, j] - v_cache[v, j]|   (fp32)
+ *   mask[v] = dist[v] > threshold
+ *
+ *   v_new     in      [rows, H, d]   (dtype)     v_cache  in/out  [rows, H, d]
+ *   threshold         >= 0 (or +inf); the page gives no value, so the caller chooses it
+ *   mask      out     uint8 [rows, H]: 1 active, 0 not (16-byte aligned)
+ *   active_idx out    int32 [rows * H] capacity, or NULL: the first *n_active entries are
+ *                     the flat indices r * H + h of the active vectors, increasing within
+ *                     each run of 1024 vectors, runs in unspecified order
+ *   n_active  out     device int64: number of active vectors (8-byte aligned)
+ *   update_cache      nonzero: v_cache rows of active vectors are overwritten with v_new
+ * d * element size must be a multiple of 16 bytes and at most 512 (bf16 d % 8 == 0,
+ * d <= 256; fp32 d % 4 == 0, d <= 128).  Outputs must not overlap inputs or each other;
+ * v_new and v_cache must not overlap.  The whole-step refresh the page describes (every
+ * 10 steps, all vectors) is the caller's: pass threshold 0 or copy v_new.
+ */
+st_status st_v_change(const void *v_new, void *v_cache, int64_t rows, int H, int d, float threshold, int dtype,
+                      uint8_t *mask, int32_t *active_idx, int64_t *n_active, int update_cache, void *stream);
+
+/*
  * st_relayout -- strided N-D copy, the one-GPU form of the spatial <-> temporal
  * redistribution (ScaleFusion review, "Technical architecture", execution flow)
  * and of the blocked rearranges and slice gathers/scatters of the algorithm

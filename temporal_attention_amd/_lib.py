@@ -24,7 +24,7 @@ ST_ROPE_NONE, ST_ROPE_1D, ST_ROPE_2D = 0, 1, 2
 EXPORTS = (
     "st_status_str", "st_rope_table_floats", "st_rope_table", "st_qkv_norm_rope", "st_out_proj",
     "st_attn_spatial", "st_attn_temporal", "st_attn_chunk", "st_attn_merge", "st_relayout", "st_block_sliced",
-    "st_block_sliced_2s", "st_block_sliced_workspace",
+    "st_block_sliced_2s", "st_block_sliced_workspace", "st_v_change",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -63,6 +63,7 @@ _SIGS = {
     "st_attn_temporal": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p, _p]),
     "st_attn_chunk": (_i, [_p, _p, _p, _i64, _i, _i, _i, _i, _i, _f, _i, _p, _p, _p]),
     "st_attn_merge": (_i, [_p, _p, _p, _p, _i64, _i, _i, _i, _i, _p, _p, _p]),
+    "st_v_change": (_i, [_p, _p, _i64, _i, _i, _f, _i, _p, _p, _p, _i, _p]),
     "st_relayout": (_i, [_p, C.POINTER(C.c_int64), _p, C.POINTER(C.c_int64), C.POINTER(C.c_int64), _i, _i, _p]),
     "st_block_sliced": (_i, [_p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, C.POINTER(st_layer_weights),
                              C.POINTER(st_layer_weights), _f, _f, _i, _p, _p, _sz, _p]),
@@ -144,6 +145,13 @@ def st_attn_chunk(q, k, v, outer, Lq, Lk, kv_valid, H, d, scale, dtype, out, lse
 def st_attn_merge(o_a, lse_a, o_b, lse_b, outer, L, H, d, dtype, out, lse, stream=None):
     _check("st_attn_merge", lib.st_attn_merge(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), outer, L, H, d, dtype,
                                               _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def st_v_change(v_new, v_cache, rows, H, d, threshold, dtype, mask, active_idx, n_active, update_cache,
+                stream=None):
+    _check("st_v_change", lib.st_v_change(_ptr(v_new), _ptr(v_cache), rows, H, d, threshold, dtype, _ptr(mask),
+                                          _ptr(active_idx), _ptr(n_active), int(bool(update_cache)),
+                                          _stream(stream)))
 
 
 def _i64arr(vals):

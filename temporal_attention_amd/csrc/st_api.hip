@@ -453,6 +453,27 @@ st_status st_attn_merge(const void *o_a, const float *lse_a, const void *o_b, co
   return launch_attn_merge(o_a, lse_a, o_b, lse_b, outer, L, H, d, (int)esize(dtype), out, lse, (hipStream_t)stream);
 }
 
+st_status st_v_change(const void *v_new, void *v_cache, int64_t rows, int H, int d, float threshold, int dtype,
+                      uint8_t *mask, int32_t *active_idx, int64_t *n_active, int update_cache, void *stream) {
+  if (!dtype_ok(dtype)) return ST_EINVAL;
+  if (!v_new || !v_cache || !mask || !n_active || rows < 0 || H < 1 || d < 1) return ST_EINVAL;
+  if (isnan(threshold) || threshold < 0.f) return ST_EINVAL;
+  const int64_t e = (int64_t)esize(dtype);
+  if ((d * e) % 16 || d * e > 512) return ST_EUNSUPPORTED;
+  const int64_t nvec = rows * H;
+  if (rows >= (1ll << 40) || nvec >= (1ll << 31)) return ST_EUNSUPPORTED;
+  if (!aligned16(v_new) || !aligned16(v_cache)) return ST_EALIGN;
+  if ((uintptr_t)n_active % 8 || (uintptr_t)active_idx % 4 || !aligned16(mask)) return ST_EALIGN;
+  const Range rn = rng(v_new, nvec * d * e), rc = rng(v_cache, nvec * d * e), rm = rng(mask, nvec),
+              ri = rng(active_idx, active_idx ? nvec * 4 : 0), rk = rng(n_active, 8);
+  if (overlap(rn, rc)) return ST_EINVAL;
+  for (const Range &o : {rm, ri, rk})
+    if (overlap(o, rn) || overlap(o, rc)) return ST_EINVAL;
+  if (overlap(rm, ri) || overlap(rm, rk) || overlap(ri, rk)) return ST_EINVAL;
+  return launch_v_change(v_new, v_cache, nvec, d, (int)e, threshold, mask, active_idx, n_active, update_cache,
+                         (hipStream_t)stream);
+}
+
 st_status st_relayout(const void *src, const int64_t *src_strides, void *dst, const int64_t *dst_strides,
                       const int64_t *dims, int ndim, int elem_bytes, void *stream) {
   if (!src || !dst || !src_strides || !dst_strides || !dims) return ST_EINVAL;

@@ -89,6 +89,12 @@ st_status launch_attn_empty(void *o, float *lse, int64_t outer, int L, int H, in
 st_status launch_attn_merge(const void *o_a, const float *lse_a, const void *o_b, const float *lse_b, int64_t outer,
                             int L, int H, int d, int elem_bytes, void *o, float *lse, hipStream_t s);
 
+// V-Major change detection: mask[v] = sum_j |v_new - v_cache| > threshold per row of d elements
+// (d * elem_bytes a multiple of 16, at most 512 bytes); active rows compacted into idx (order
+// unspecified, may be null), their count into *n_active; update != 0 refreshes the cache rows.
+st_status launch_v_change(const void *v_new, void *v_cache, int64_t nvec, int d, int elem_bytes, float threshold,
+                          uint8_t *mask, int32_t *idx, int64_t *n_active, int update, hipStream_t s);
+
 bool attn_bf16_supported(int d);
 bool attn_short_supported(int L, int d);
 

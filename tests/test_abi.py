@@ -171,6 +171,34 @@ def test_attn_merge_validation(kw, want):
     assert code(st.st_attn_merge, *merge_args(**kw)) == want
 
 
+def vchange_args(**kw):
+    a = dict(v_new=P, v_cache=P2, rows=100, H=16, d=72, threshold=1.0, dtype=st.ST_BF16, mask=BIG, active_idx=2 * BIG,
+             n_active=3 * BIG, update_cache=1)
+    a.update(kw)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(v_new=None), st.ST_EINVAL),
+    (dict(mask=None), st.ST_EINVAL),
+    (dict(n_active=None), st.ST_EINVAL),
+    (dict(threshold=-1.0), st.ST_EINVAL),
+    (dict(threshold=float("nan")), st.ST_EINVAL),
+    (dict(H=0), st.ST_EINVAL),
+    (dict(dtype=4), st.ST_EINVAL),
+    (dict(d=70), st.ST_EUNSUPPORTED),                # rows must be whole 16-byte pieces
+    (dict(d=264), st.ST_EUNSUPPORTED),               # more than 512 bytes per row
+    (dict(v_cache=P + 64), st.ST_EINVAL),            # v_new and v_cache overlap
+    (dict(mask=P2 + 16), st.ST_EINVAL),              # mask inside v_cache
+    (dict(active_idx=BIG + 16), st.ST_EINVAL),       # idx overlaps mask
+    (dict(v_new=P + 8), st.ST_EALIGN),
+    (dict(n_active=3 * BIG + 4), st.ST_EALIGN),
+    (dict(mask=BIG + 1), st.ST_EALIGN),
+])
+def test_v_change_validation(kw, want):
+    assert code(st.st_v_change, *vchange_args(**kw)) == want
+
+
 def test_relayout_validation():
     dims, s1, s2 = [2, 3, 4], [12, 4, 1], [12, 1, 3]
     assert code(st.st_relayout, None, s1, BIG, s2, dims, 3, 2) == st.ST_EINVAL
