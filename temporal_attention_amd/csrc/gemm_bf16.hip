@@ -224,17 +224,23 @@ __device__ __forceinline__ void epilogue_qkv(const GemmArgs &a, f32x4 (&acc)[CT]
   const int gh0 = nw0 / D;   // global head index (over 3H) of the wave's first head
   const int npairs = a.rope.kind == ST_ROPE_2D ? D / 4 : D / 2;
 
+  // Pass 1, per token row of the lane: 1 / RMS of each head of the wave, and
+  // the token's RoPE position.  A lane's 4 channels of one MFMA tile belong to
+  // one head; the head's sum of squares is completed over the 4 lanes that
+  // share the token (lane groups 16 apart).
+  float inv[kTT][HPW];
+  int p0[kTT], p1[kTT];
+  int64_t roff[kTT];         // element offset of the lane's token row in q, k, v; -1: past the last row
+  const uint32_t period = (uint32_t)min<int64_t>(a.rope.period, 1ll << 30);
+  const uint32_t base_i = a.rope.kind == ST_ROPE_NONE ? 0u : (uint32_t)(m0 % a.rope.period);   // one per workgroup
 #pragma unroll
   for (int tt = 0; tt < kTT; ++tt) {
-    const int64_t r = m0 + wm * kWM + tt * 16 + l16;
-    // per-head sum of squares over this lane's channels, then over the 4 lanes of the token
     float ss[HPW];
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) ss[hh] = 0.f;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
-      const int cl = ct * 16 + g4 * 4;
-      const int hh = cl / D;
+      const int hh = (ct * 16 + g4 * 4) / D;
       float s4 = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) s4 += acc[ct][tt][j] * acc[ct][tt][j];
@@ -245,61 +251,61 @@ __device__ __forceinline__ void epilogue_qkv(const GemmArgs &a, f32x4 (&acc)[CT]
     for (int hh = 0; hh < HPW; ++hh) {
       ss[hh] += __shfl_xor(ss[hh], 16);
       ss[hh] += __shfl_xor(ss[hh], 32);
+      inv[tt][hh] = rsqrtf(ss[hh] * (1.0f / D) + a.eps);
     }
-    if (r >= a.M) continue;
-    // position of this token
-    int p0 = 0, p1 = 0;
+    const int64_t r = m0 + wm * kWM + tt * 16 + l16;
+    roff[tt] = r < a.M ? r * hd : -1;
+    p0[tt] = p1[tt] = 0;
     if (a.rope.kind != ST_ROPE_NONE) {
-      const int64_t i = r % a.rope.period + a.rope.offset;
+      const uint32_t i = (base_i + (uint32_t)(wm * kWM + tt * 16 + l16)) % period + (uint32_t)a.rope.offset;
       if (a.rope.kind == ST_ROPE_1D) {
-        p0 = (int)i;
+        p0[tt] = (int)i;
       } else {
-        p0 = (int)(i / a.rope.grid_w);
-        p1 = (int)(i % a.rope.grid_w);
+        p0[tt] = (int)(i / (uint32_t)a.rope.grid_w);
+        p1[tt] = (int)(i - (uint32_t)p0[tt] * (uint32_t)a.rope.grid_w);
       }
     }
+  }
+
+  // Pass 2, channel tile outer: the tile's head, section (q, k, v), gains and
+  // rotation pair are fixed for all token rows.  v heads skip the arithmetic
+  // by select, so there is no divergent branch.
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      const int cl = ct * 16 + g4 * 4;
-      const int hh = cl / D;
-      const int gh = gh0 + hh;
-      if (gh >= 3 * H) continue;
-      const int which = gh / H;              // 0 q, 1 k, 2 v
-      const int jd = cl - hh * D;            // dim within the head (multiple of 4)
-      float o[4] = {acc[ct][tt][0], acc[ct][tt][1], acc[ct][tt][2], acc[ct][tt][3]};
-      if (which < 2) {
-        float sh = 0.f;
+  for (int ct = 0; ct < CT; ++ct) {
+    const int cl = ct * 16 + g4 * 4;
+    const int hh = cl / D;
+    const int gh = gh0 + hh;
+    if (gh >= 3 * H) continue;
+    const int which = gh / H;              // 0 q, 1 k, 2 v
+    const int jd = cl - hh * D;            // dim within the head (multiple of 4)
+    const bool norm = which < 2;
+    const float4 g = *reinterpret_cast<const float4 *>((which == 0 ? a.g_q : a.g_k) + jd);
+    const bool second = a.rope.kind == ST_ROPE_2D && jd >= D / 2;
+    const int pair = (jd - (second ? D / 2 : 0)) >> 1;
+    u16 *dst = (which == 0 ? a.q : (which == 1 ? a.k : a.v)) + (gh - which * H) * D + jd;
 #pragma unroll
-        for (int h2 = 0; h2 < HPW; ++h2) sh = (hh == h2) ? ss[h2] : sh;
-        const float inv = rsqrtf(sh * (1.0f / D) + a.eps);
-        const float4 g = *reinterpret_cast<const float4 *>((which == 0 ? a.g_q : a.g_k) + jd);
-        o[0] *= inv * g.x;
-        o[1] *= inv * g.y;
-        o[2] *= inv * g.z;
-        o[3] *= inv * g.w;
-        if (a.rope.kind != ST_ROPE_NONE) {
-          int pos, pair;
-          if (a.rope.kind == ST_ROPE_1D) {
-            pos = p0;
-            pair = jd >> 1;
-          } else {
-            const bool second = jd >= D / 2;
-            pos = second ? p1 : p0;
-            pair = (jd - (second ? D / 2 : 0)) >> 1;
-          }
-          const float4 cs = *reinterpret_cast<const float4 *>(a.rope.table + ((int64_t)pos * npairs + pair) * 2);
-          const float x0 = o[0], x1 = o[1], x2 = o[2], x3 = o[3];
-          o[0] = x0 * cs.x - x1 * cs.y;
-          o[1] = x0 * cs.y + x1 * cs.x;
-          o[2] = x2 * cs.z - x3 * cs.w;
-          o[3] = x2 * cs.w + x3 * cs.z;
-        }
+    for (int tt = 0; tt < kTT; ++tt) {
+      if (roff[tt] < 0) continue;
+      float invh = inv[tt][0];
+#pragma unroll
+      for (int h2 = 1; h2 < HPW; ++h2) invh = hh == h2 ? inv[tt][h2] : invh;
+      float o[4] = {acc[ct][tt][0] * invh * g.x, acc[ct][tt][1] * invh * g.y, acc[ct][tt][2] * invh * g.z,
+                    acc[ct][tt][3] * invh * g.w};
+      if (a.rope.kind != ST_ROPE_NONE) {
+        const int pos = second ? p1[tt] : p0[tt];
+        const float4 cs = *reinterpret_cast<const float4 *>(a.rope.table + ((int64_t)pos * npairs + pair) * 2);
+        const float x0 = o[0], x1 = o[1], x2 = o[2], x3 = o[3];
+        o[0] = x0 * cs.x - x1 * cs.y;
+        o[1] = x0 * cs.y + x1 * cs.x;
+        o[2] = x2 * cs.z - x3 * cs.w;
+        o[3] = x2 * cs.w + x3 * cs.z;
       }
-      u16 *dst = which == 0 ? a.q : (which == 1 ? a.k : a.v);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = norm ? o[j] : acc[ct][tt][j];
       uint2 ov;
       ov.x = pack_bf16x2(o[0], o[1]);
       ov.y = pack_bf16x2(o[2], o[3]);
-      *reinterpret_cast<uint2 *>(dst + r * hd + (gh - which * H) * D + jd) = ov;
+      *reinterpret_cast<uint2 *>(dst + roff[tt]) = ov;
     }
   }
 }
