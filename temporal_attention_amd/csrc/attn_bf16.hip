@@ -20,11 +20,12 @@
 // (three 32-row tiles); the spare row 72 of V^T is filled with ones, so row
 // 72 of O^T accumulates the softmax denominator in the same MFMAs.
 //
-// Long sequences (attn_long_kernel): a workgroup of 4 waves owns 32*NT
-// queries per wave; K and V^T tiles of 64 keys are staged through a
-// double-buffered LDS stage (V transposed on the way in), and the online
-// softmax only rescales the accumulator when a query's running maximum grows
-// by more than 8 (in log2 units), so exponentials stay <= 2^8 in between.
+// Long sequences (attn_long_kernel): a workgroup of 8 waves owns 32*NT
+// queries per wave; K and V tiles of 128 keys (64 for d = 128) go from
+// global memory straight into three rotating LDS stages, V^T is read from
+// them with transpose reads, and the online softmax only rescales the
+// accumulator when a query's running maximum grows by more than 8 (in log2
+// units), so exponentials stay <= 2^8 in between.
 // Short sequences (attn_short_kernel, L <= 64): one wave per (outer, head)
 // loads its whole Q and K straight into operand registers and V^T through a
 // private LDS slice; a workgroup covers all heads of one outer index, which
@@ -123,6 +124,12 @@ __device__ __forceinline__ float max_across_halves(float x) {
 __device__ __forceinline__ int acc_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
 
 constexpr float kRescale = 8.0f;   // log2 growth of the running max that forces a rescale
+// Keys per LDS tile of the long kernel for d <= 72: one workgroup barrier per
+// tile, so larger tiles mean fewer barriers (d = 128 keeps 64 keys so three
+// stages fit in LDS).
+#ifndef ST_KB
+#define ST_KB 128
+#endif
 #ifndef ST_LONG_WAVES
 #define ST_LONG_WAVES 8
 #endif
@@ -138,7 +145,7 @@ template <int D, int NT, int W = kLongWaves>
 struct LongCfg {
   typedef Dims<D> DM;
   static constexpr int WAVES = W;                 // waves per workgroup
-  static constexpr int KB = 64;                   // keys per LDS tile
+  static constexpr int KB = D <= 72 ? ST_KB : 64;  // keys per LDS tile
   static constexpr int QW = 32 * NT;              // queries per wave
   static constexpr int QB = WAVES * QW;           // queries per workgroup
   static constexpr int TILE = KB * D;             // u16 per K or V tile: rows packed as in memory
@@ -392,13 +399,13 @@ struct LongWave {
   // slot.  Steps alternate slots, so no scores are ever copied.  Phase nt
   // pairs the S^T MFMAs of query tile nt of unit un with the exponentials of
   // the same tile of unit u, so only one tile of each is in flight at once;
-  // the last phase pairs O^T += V^T P^T with the rescale test.
-  template <bool NEXT, int CUR>
-  __device__ __forceinline__ void step(f32x16 (&sb)[2][NT], const u16 *__restrict__ Vs,
-                                       const u16 *__restrict__ Kn, int un, bool mask_next) {
+  // the last phase pairs O^T += V^T P^T with the rescale test.  With PREF the
+  // K operand of unit up is read into kf after P.V, one step before the
+  // S^T MFMAs that use it, so that read's latency is off the critical path.
+  template <bool NEXT, int CUR, bool PREF>
+  __device__ __forceinline__ void step(f32x16 (&sb)[2][NT], bf16x8 (&kf)[DM::KS], const u16 *__restrict__ Vs, int un,
+                                       bool mask_next, const u16 *__restrict__ Kp, int up) {
     bf16x8 pf[2][NT];
-    bf16x8 kf[DM::KS];
-    if constexpr (NEXT) kfrag(kf, Kn, un);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       if constexpr (NEXT) qk(sb[CUR ^ 1][nt], kf, nt);
@@ -406,6 +413,7 @@ struct LongWave {
       __builtin_amdgcn_sched_barrier(0);
     }
     pv(pf, Vs);
+    if constexpr (PREF) kfrag(kf, Kp, up);
     if constexpr (NEXT) {
       if constexpr (!FOLD)
         if (mask_next) mask(sb[CUR ^ 1], un);
@@ -508,12 +516,13 @@ __global__ void __launch_bounds__(64 * kLongWaves, 8 / kLongWaves) attn_long_ker
     w.vconst = (gi == D % 32) ? 0x3F803F80u : 0u;
   }
 
-  // Units of 32 keys up to n_valid (later keys carry no weight), two per
-  // 64-key LDS tile.  Tiles rotate through NSTAGE stages: tile j+1 is in
-  // flight while tile j is read, and the step that finishes tile j-1's V
-  // reads runs after the barrier that opens tile j.
+  // Units of 32 keys up to n_valid (later keys carry no weight), KB / 32 per
+  // LDS tile.  Tiles rotate through NSTAGE stages: tile j+1 is in flight
+  // while tile j is read, and tile j+2 is issued into tile j-1's stage once
+  // the barrier that opens tile j has passed.
+  constexpr int UPT = C::KB / 32;   // 32-key units per tile
   const int nu = (w.nv + 31) / 32;
-  const int ntl = (nu + 1) / 2;
+  const int ntl = (nu + UPT - 1) / UPT;
   const bool partial = (w.nv & 31) != 0;
   LongDma<D> dma;
   dma.init(rs, lane, wave);
@@ -523,37 +532,48 @@ __global__ void __launch_bounds__(64 * kLongWaves, 8 / kLongWaves) attn_long_ker
   __syncthreads();
   if (ntl > 1) dma.issue(lds + C::STAGE, C::KB, kp, vp, rs, Lk, lane, wave);
 
+  // K (and, + REGION, V) rows of unit u
+  auto unit_rows = [&](int u) { return lds + ((u / UPT) % C::NSTAGE) * C::STAGE + (u % UPT) * 32 * D; };
   f32x16 sb[2][NT];
+  bf16x8 kf[DM::KS];
   {
-    w.qk(sb[0], lds, 0);
+    w.kfrag(kf, lds, 0);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) w.qk(sb[0][nt], kf, nt);
     if constexpr (!W::FOLD)
       if (partial && nu == 1) w.mask(sb[0], 0);
     float lm[NT];
     w.needs_rescale(sb[0], lm);
     w.rescale(sb[0], lm, true);
+    if (nu > 1) w.kfrag(kf, lds + 32 * D, 1);
   }
 
-  int st = 0;   // stage of tile kt
-  for (int kt = 0; kt + 1 < ntl; ++kt) {
-    const u16 *Ks = lds + st * C::STAGE;
-    const u16 *Vs = Ks + C::REGION;
-    const int st1 = st == C::NSTAGE - 1 ? 0 : st + 1;
-    const int st2 = st1 == C::NSTAGE - 1 ? 0 : st1 + 1;
-    w.template step<true, 0>(sb, Vs, Ks + 32 * D, 2 * kt + 1, partial && 2 * kt + 1 == nu - 1);
-    wait_vmem();
-    __syncthreads();
-    if (kt + 2 < ntl) dma.issue(lds + st2 * C::STAGE, (kt + 2) * C::KB, kp, vp, rs, Lk, lane, wave);
-    w.template step<true, 1>(sb, Vs + 32 * D, lds + st1 * C::STAGE, 2 * kt + 2, partial && 2 * kt + 2 == nu - 1);
-    st = st1;
+  // Units in pairs; one barrier per tile, at the top of its first pair:
+  // tile kt+1 has landed (K is read one unit ahead, possibly from it) and
+  // tile kt-1's stage is free for tile kt+2.
+  int p = 0;
+  for (; 2 * p + 2 < nu; ++p) {
+    const int u = 2 * p;
+    if (u % UPT == 0) {
+      const int kt = u / UPT;
+      wait_vmem();
+      __syncthreads();
+      if (kt + 2 < ntl) dma.issue(lds + ((kt + 2) % C::NSTAGE) * C::STAGE, (kt + 2) * C::KB, kp, vp, rs, Lk, lane, wave);
+    }
+    w.template step<true, 0, true>(sb, kf, unit_rows(u) + C::REGION, u + 1, partial && u + 1 == nu - 1,
+                                   unit_rows(u + 2), u + 2);
+    w.template step<true, 1, true>(sb, kf, unit_rows(u + 1) + C::REGION, u + 2, partial && u + 2 == nu - 1,
+                                   unit_rows(u + 3), u + 3);
   }
   {
-    const u16 *Ks = lds + st * C::STAGE;
-    const u16 *Vs = Ks + C::REGION;
-    if (2 * ntl == nu) {
-      w.template step<true, 0>(sb, Vs, Ks + 32 * D, nu - 1, partial);
-      w.template step<false, 1>(sb, Vs + 32 * D, nullptr, 0, false);
+    // the last one or two units: their tile has landed (waited at the previous
+    // tile's barrier, or before the loop), and nothing is prefetched
+    const int u = 2 * p;
+    if (u + 2 == nu) {
+      w.template step<true, 0, false>(sb, kf, unit_rows(u) + C::REGION, u + 1, partial, nullptr, 0);
+      w.template step<false, 1, false>(sb, kf, unit_rows(u + 1) + C::REGION, 0, false, nullptr, 0);
     } else {
-      w.template step<false, 0>(sb, Vs, nullptr, 0, false);
+      w.template step<false, 0, false>(sb, kf, unit_rows(u) + C::REGION, 0, false, nullptr, 0);
     }
   }
 
