@@ -123,6 +123,22 @@ st_status st_out_proj(const void *a, int64_t rows, int k_in, const void *w, int 
                       int dtype, void *y, void *stream);
 
 /*
+ * st_out_proj_relayout -- st_out_proj with the spatial <-> temporal relayout
+ * (ScaleFusion review, "Technical architecture", execution flow) fused into
+ * its stores: the rows of a, taken as [outer, n1, n2], are written to y as
+ * [outer, n2, n1].  n1 = T, n2 = S turns the spatial layer's [B, T, S, C]
+ * output into the temporal layer's [B, S, T, C] input; n1 = S, n2 = T turns
+ * it back.  Every output element is bit-identical to st_out_proj followed by
+ * st_relayout of the same rows; the relayout costs no extra pass over HBM.
+ *
+ *   a  in  [rows, k_in]   w in [n_out, k_in]   y out [rows, n_out]   (dtype)
+ *   n1, n2 >= 1, rows a multiple of n1 * n2 (else ST_EINVAL; rows may be 0).
+ * bf16: k_in must be a multiple of 64.  n_out must be a multiple of 4.
+ */
+st_status st_out_proj_relayout(const void *a, int64_t rows, int k_in, const void *w, int n_out,
+                               int dtype, int64_t n1, int64_t n2, void *y, void *stream);
+
+/*
  * st_attn_spatial -- spatial attention: for every (b, t, h),
  *   O = softmax(Q K^T * scale) V over the S patch tokens of frame t.
  * ScaleFusion review, "Technical architecture" (the spatial layer attends over

@@ -23,8 +23,8 @@ ST_ROPE_NONE, ST_ROPE_1D, ST_ROPE_2D = 0, 1, 2
 # Every entry point declared in include/st.h.
 EXPORTS = (
     "st_status_str", "st_rope_table_floats", "st_rope_table", "st_qkv_norm_rope", "st_out_proj",
-    "st_attn_spatial", "st_attn_temporal", "st_attn_chunk", "st_attn_merge", "st_relayout", "st_block_sliced",
-    "st_block_sliced_2s", "st_block_sliced_workspace", "st_v_change",
+    "st_out_proj_relayout", "st_attn_spatial", "st_attn_temporal", "st_attn_chunk", "st_attn_merge", "st_relayout",
+    "st_block_sliced", "st_block_sliced_2s", "st_block_sliced_workspace", "st_v_change",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -59,6 +59,7 @@ _SIGS = {
     "st_qkv_norm_rope": (_i, [_p, _i64, _i, _p, _p, _p, _f, _i, _p, _i, _i64, _i64, _i, _i, _i, _i, _p, _p, _p,
                               _p]),
     "st_out_proj": (_i, [_p, _i64, _i, _p, _i, _i, _p, _p]),
+    "st_out_proj_relayout": (_i, [_p, _i64, _i, _p, _i, _i, _i64, _i64, _p, _p]),
     "st_attn_spatial": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p, _p]),
     "st_attn_temporal": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p, _p]),
     "st_attn_chunk": (_i, [_p, _p, _p, _i64, _i, _i, _i, _i, _i, _f, _i, _p, _p, _p]),
@@ -125,6 +126,11 @@ def st_qkv_norm_rope(x, rows, c_in, w_qkv, g_q, g_k, eps, rope_kind, rope_table,
 
 def st_out_proj(a, rows, k_in, w, n_out, dtype, y, stream=None):
     _check("st_out_proj", lib.st_out_proj(_ptr(a), rows, k_in, _ptr(w), n_out, dtype, _ptr(y), _stream(stream)))
+
+
+def st_out_proj_relayout(a, rows, k_in, w, n_out, dtype, n1, n2, y, stream=None):
+    _check("st_out_proj_relayout", lib.st_out_proj_relayout(_ptr(a), rows, k_in, _ptr(w), n_out, dtype, n1, n2,
+                                                            _ptr(y), _stream(stream)))
 
 
 def st_attn_spatial(q, k, v, B, T, S, H, d, scale, dtype, out, stream=None):

@@ -50,7 +50,8 @@ struct GemmArgs {
   int64_t M;
   int K, N;
   // plain output
-  u16 *y;            // [M, N]
+  u16 *y;            // [M, N], rows permuted by sw
+  RowSwap sw;
   // qkv output
   u16 *q, *k, *v;    // [M, H, D]
   int H;
@@ -197,6 +198,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_bf16_kernel(GemmArgs a, uint
     for (int tt = 0; tt < kTT; ++tt) {
       const int64_t r = m0 + wm * kWM + tt * 16 + l16;
       if (r >= a.M) continue;
+      u16 *yr = a.y + swap_row(r, a.sw) * a.N;
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
         const int n = nw0 + ct * 16 + g4 * 4;
@@ -204,7 +206,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_bf16_kernel(GemmArgs a, uint
         uint2 o;
         o.x = pack_bf16x2(acc[ct][tt][0], acc[ct][tt][1]);
         o.y = pack_bf16x2(acc[ct][tt][2], acc[ct][tt][3]);
-        *reinterpret_cast<uint2 *>(a.y + r * a.N + n) = o;
+        *reinterpret_cast<uint2 *>(yr + n) = o;
       }
     }
   } else {
@@ -349,7 +351,7 @@ st_status launch_qkv_bf16(const void *x, int64_t rows, int c_in, const void *w, 
 }
 
 st_status launch_linear_bf16(const void *a_, int64_t rows, int k_in, const void *w, int n_out, void *y,
-                             hipStream_t s) {
+                             hipStream_t s, RowSwap sw) {
   GemmArgs a{};
   a.x = static_cast<const u16 *>(a_);
   a.w = static_cast<const u16 *>(w);
@@ -357,6 +359,7 @@ st_status launch_linear_bf16(const void *a_, int64_t rows, int k_in, const void 
   a.K = k_in;
   a.N = n_out;
   a.y = static_cast<u16 *>(y);
+  a.sw = sw;
   if (n_out % 288 == 0) return launch_gemm<9, 0, 0>(a, s);
   return launch_gemm<8, 0, 0>(a, s);
 }

@@ -49,9 +49,10 @@ st_status do_qkv(const void *x, int64_t rows, int c_in, const void *w, const flo
                         (float *)k, (float *)v, s);
 }
 
-st_status do_linear(const void *a, int64_t rows, int k_in, const void *w, int n_out, int dt, void *y, hipStream_t s) {
-  if (dt == ST_BF16) return launch_linear_bf16(a, rows, k_in, w, n_out, y, s);
-  return launch_linear_f32((const float *)a, rows, k_in, (const float *)w, n_out, (float *)y, s);
+st_status do_linear(const void *a, int64_t rows, int k_in, const void *w, int n_out, int dt, void *y, hipStream_t s,
+                    RowSwap sw = {}) {
+  if (dt == ST_BF16) return launch_linear_bf16(a, rows, k_in, w, n_out, y, s, sw);
+  return launch_linear_f32((const float *)a, rows, k_in, (const float *)w, n_out, (float *)y, s, sw);
 }
 
 st_status do_attn(const void *q, const void *k, const void *v, int64_t outer, int L, int nv, int H, int d, float scale,
@@ -94,8 +95,7 @@ BlockPlan plan_block(int B, int T, int S, int grid_w, int C, int H, int d, int n
     p.xs = take(rows * C * e);
     p.xs2 = take(rows * C * e);   // slice buffers are double-buffered (two-stream pipeline)
   } else {
-    p.hb = take(N * C * e);   // spatial output [B,T,S,C], later the temporal output [B,S,T,C]
-    p.xs = take(N * C * e);   // [B,S,T,C] input of the temporal layer
+    p.xs = take(N * C * e);   // [B,S,T,C] input of the temporal layer (the spatial output, relayout fused)
     rows = N;
   }
   p.q = take(rows * hd * e);
@@ -108,16 +108,17 @@ BlockPlan plan_block(int B, int T, int S, int grid_w, int C, int H, int d, int n
   return p;
 }
 
-// One layer: projection + norm/RoPE, attention, output projection.
+// One layer: projection + norm/RoPE, attention, output projection (its rows
+// optionally stored in swapped order, which fuses the following relayout).
 st_status run_layer(const void *x, int64_t outer, int L, int nv, int C, int H, int d, const st_layer_weights *w,
                     float eps, const RopeArgs &rope, int dt, void *q, void *k, void *v, void *o, void *y,
-                    bool temporal, hipStream_t s) {
+                    bool temporal, hipStream_t s, RowSwap sw = {}) {
   const int64_t rows = outer * L;
   st_status r = do_qkv(x, rows, C, w->w_qkv, w->g_q, w->g_k, eps, rope, H, d, dt, q, k, v, s);
   if (r != ST_OK) return r;
   r = do_attn(q, k, v, outer, L, nv, H, d, (float)(1.0 / sqrt((double)d)), dt, o, temporal, s);
   if (r != ST_OK) return r;
-  return do_linear(o, rows, H * d, w->w_o, C, dt, y, s);
+  return do_linear(o, rows, H * d, w->w_o, C, dt, y, s, sw);
 }
 
 // Events that order the two streams of the pipelined slicing schedule.  A
@@ -219,22 +220,14 @@ st_status block_sliced(const void *x, int B, int T, int t_valid, int S, int grid
   const int64_t Cl = C;
 
   if (n_t == 1 && n_s == 1) {
-    void *h = W + P.hb, *hs = W + P.xs;
-    r = run_layer(x, (int64_t)B * T, S, S, C, H, d, spatial, eps, r2, dtype, q, k, v, o, h, false, s);
+    // Both relayouts ride on the output projections: the spatial layer's
+    // rows (b, t, s) are stored as rows (b, s, t) of the temporal input, and
+    // the temporal layer's rows (b, s, t) as rows (b, t, s) of y.
+    void *hs = W + P.xs;
+    r = run_layer(x, (int64_t)B * T, S, S, C, H, d, spatial, eps, r2, dtype, q, k, v, o, hs, false, s, RowSwap{T, S});
     if (r != ST_OK) return r;
-    {  // [B,T,S,C] -> [B,S,T,C]
-      const int64_t dims[4] = {B, T, S, C};
-      const int64_t ss[4] = {(int64_t)T * S * Cl, S * Cl, Cl, 1};
-      const int64_t ds[4] = {(int64_t)S * T * Cl, Cl, T * Cl, 1};
-      r = launch_relayout(h, ss, hs, ds, dims, 4, eb, s);
-      if (r != ST_OK) return r;
-    }
-    r = run_layer(hs, (int64_t)B * S, T, t_valid, C, H, d, temporal, eps, r1, dtype, q, k, v, o, h, true, s);
-    if (r != ST_OK) return r;
-    const int64_t dims[4] = {B, S, T, C};   // [B,S,T,C] -> [B,T,S,C]
-    const int64_t ss[4] = {(int64_t)S * T * Cl, T * Cl, Cl, 1};
-    const int64_t ds[4] = {(int64_t)T * S * Cl, Cl, S * Cl, 1};
-    return launch_relayout(h, ss, y, ds, dims, 4, eb, s);
+    return run_layer(hs, (int64_t)B * S, T, t_valid, C, H, d, temporal, eps, r1, dtype, q, k, v, o, y, true, s,
+                     RowSwap{S, T});
   }
 
   // Sliced schedule.  Blocked layout xb[b][i][j][a][e][c] with a < T/N_T, e < S/N_S.
@@ -376,6 +369,20 @@ st_status st_out_proj(const void *a, int64_t rows, int k_in, const void *w, int 
   const Range ry = rng(y, rows * n_out * e);
   if (overlap(ry, rng(a, rows * k_in * e)) || overlap(ry, rng(w, (int64_t)n_out * k_in * e))) return ST_EINVAL;
   return do_linear(a, rows, k_in, w, n_out, dtype, y, (hipStream_t)stream);
+}
+
+st_status st_out_proj_relayout(const void *a, int64_t rows, int k_in, const void *w, int n_out, int dtype,
+                               int64_t n1, int64_t n2, void *y, void *stream) {
+  if (n1 < 1 || n2 < 1 || n1 >= (1ll << 31) || n2 >= (1ll << 31) || rows < 0 || rows % (n1 * n2)) return ST_EINVAL;
+  if (!dtype_ok(dtype)) return ST_EINVAL;
+  if (!a || !w || !y || k_in < 1 || n_out < 1) return ST_EINVAL;
+  if (n_out % 4 || (dtype == ST_BF16 && k_in % 64)) return ST_EUNSUPPORTED;
+  if (rows >= (1ll << 40) || (int64_t)k_in * n_out >= (1ll << 40)) return ST_EUNSUPPORTED;
+  if (!aligned16(a) || !aligned16(w) || !aligned16(y)) return ST_EALIGN;
+  const size_t e = esize(dtype);
+  const Range ry = rng(y, rows * n_out * e);
+  if (overlap(ry, rng(a, rows * k_in * e)) || overlap(ry, rng(w, (int64_t)n_out * k_in * e))) return ST_EINVAL;
+  return do_linear(a, rows, k_in, w, n_out, dtype, y, (hipStream_t)stream, RowSwap{n1, n2});
 }
 
 static st_status attn_common(const void *q, const void *k, const void *v, int64_t outer, int L, int nv, int H, int d,

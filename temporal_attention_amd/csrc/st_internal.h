@@ -62,13 +62,26 @@ struct RopeArgs {
 st_status launch_qkv_bf16(const void *x, int64_t rows, int c_in, const void *w, const float *g_q,
                           const float *g_k, float eps, const RopeArgs &rope, int H, int d, void *q,
                           void *k, void *v, hipStream_t s);
+// Output rows of a linear layer written in swapped order: rows in [outer, n1, n2]
+// order go to [outer, n2, n1]; n1 = 0 writes rows in place.
+struct RowSwap {
+  int64_t n1 = 0, n2 = 0;
+};
+__host__ __device__ inline int64_t swap_row(int64_t r, RowSwap sw) {
+  if (sw.n1 == 0) return r;
+  const int64_t blk = sw.n1 * sw.n2;
+  const int64_t o = r / blk, rem = r - o * blk;
+  const int64_t i = rem / sw.n2, j = rem - i * sw.n2;
+  return o * blk + j * sw.n1 + i;
+}
+
 st_status launch_linear_bf16(const void *a, int64_t rows, int k_in, const void *w, int n_out, void *y,
-                             hipStream_t s);
+                             hipStream_t s, RowSwap sw = {});
 st_status launch_qkv_f32(const float *x, int64_t rows, int c_in, const float *w, const float *g_q,
                          const float *g_k, float eps, const RopeArgs &rope, int H, int d, float *q,
                          float *k, float *v, hipStream_t s);
 st_status launch_linear_f32(const float *a, int64_t rows, int k_in, const float *w, int n_out, float *y,
-                            hipStream_t s);
+                            hipStream_t s, RowSwap sw = {});
 
 // Attention over the middle axis L of [outer, L, H, d] tensors, keys j >= n_valid masked.
 st_status launch_attn_bf16(const void *q, const void *k, const void *v, int64_t outer, int L, int n_valid,

@@ -4,14 +4,16 @@ This is the same launch sequence st_block_sliced runs natively for
 n_t = n_s = 1, exposed step by step so that callers can time or inspect each
 kernel: torch provides the device buffers, every step is one libst.so call.
 
-    qkv_spatial     st_qkv_norm_rope   x [B,T,S,C] -> q, k, v   (2D RoPE, (h, w) of s)
-    attn_spatial    st_attn_spatial    q, k, v -> o             (over S per frame)
-    proj_spatial    st_out_proj        o -> h [B,T,S,C]
-    relayout_fwd    st_relayout        h -> hs [B,S,T,C]
-    qkv_temporal    st_qkv_norm_rope   hs -> q, k, v            (1D RoPE, t)
-    attn_temporal   st_attn_temporal   q, k, v -> o             (over T per patch)
-    proj_temporal   st_out_proj        o -> h (as [B,S,T,C])
-    relayout_bwd    st_relayout        h -> y [B,T,S,C]
+    qkv_spatial     st_qkv_norm_rope      x [B,T,S,C] -> q, k, v   (2D RoPE, (h, w) of s)
+    attn_spatial    st_attn_spatial       q, k, v -> o             (over S per frame)
+    proj_spatial    st_out_proj_relayout  o -> hs [B,S,T,C]        (relayout fused into the stores)
+    qkv_temporal    st_qkv_norm_rope      hs -> q, k, v            (1D RoPE, t)
+    attn_temporal   st_attn_temporal      q, k, v -> o             (over T per patch)
+    proj_temporal   st_out_proj_relayout  o -> y [B,T,S,C]         (relayout fused into the stores)
+
+With fused=False the two relayouts are separate st_relayout passes
+(proj_* = st_out_proj into h, then relayout_fwd / relayout_bwd); the results
+are bit-identical.
 """
 from __future__ import annotations
 
@@ -49,13 +51,28 @@ class LayerPair:
         """spatial / temporal: dicts of device tensors w_qkv, w_o, g_q, g_k."""
         self.ws, self.wt = spatial, temporal
 
-    def steps(self, x):
+    def steps(self, x, fused=True):
         """[(name, thunk)] for one pass over x ([B,T,S,C] device tensor)."""
         B, T, S, C, H, d, N, dt = self.B, self.T, self.S, self.C, self.H, self.d, self.N, self.dtype
         ws, wt = self.ws, self.wt
         eb = 2 if dt == L.ST_BF16 else 4
         fwd = ([B, T, S, C], [T * S * C, S * C, C, 1], [S * T * C, C, T * C, 1])
         bwd = ([B, S, T, C], [S * T * C, T * C, C, 1], [T * S * C, C, S * C, 1])
+        if fused:
+            return [
+                ("qkv_spatial", lambda: L.st_qkv_norm_rope(
+                    x, N, C, ws["w_qkv"], ws["g_q"], ws["g_k"], self.eps, L.ST_ROPE_2D, self.rope2, self.npos2, S, 0,
+                    self.grid_w, H, d, dt, self.q, self.k, self.v)),
+                ("attn_spatial", lambda: L.st_attn_spatial(self.q, self.k, self.v, B, T, S, H, d, self.scale, dt,
+                                                           self.o)),
+                ("proj_spatial", lambda: L.st_out_proj_relayout(self.o, N, self.hd, ws["w_o"], C, dt, T, S, self.hs)),
+                ("qkv_temporal", lambda: L.st_qkv_norm_rope(
+                    self.hs, N, C, wt["w_qkv"], wt["g_q"], wt["g_k"], self.eps, L.ST_ROPE_1D, self.rope1, T, T, 0, 0,
+                    H, d, dt, self.q, self.k, self.v)),
+                ("attn_temporal", lambda: L.st_attn_temporal(self.q, self.k, self.v, B, S, T, self.t_valid, H, d,
+                                                             self.scale, dt, self.o)),
+                ("proj_temporal", lambda: L.st_out_proj_relayout(self.o, N, self.hd, wt["w_o"], C, dt, S, T, self.y)),
+            ]
         return [
             ("qkv_spatial", lambda: L.st_qkv_norm_rope(
                 x, N, C, ws["w_qkv"], ws["g_q"], ws["g_k"], self.eps, L.ST_ROPE_2D, self.rope2, self.npos2, S, 0,
@@ -72,7 +89,7 @@ class LayerPair:
             ("relayout_bwd", lambda: L.st_relayout(self.h, bwd[1], self.y, bwd[2], bwd[0], 4, eb)),
         ]
 
-    def run(self, x):
-        for _, fn in self.steps(x):
+    def run(self, x, fused=True):
+        for _, fn in self.steps(x, fused):
             fn()
         return self.y

@@ -104,6 +104,22 @@ def test_out_proj_validation(args, want):
 
 
 @pytest.mark.parametrize("args,want", [
+    ((P, 12, 1152, P2, 1152, st.ST_BF16, 0, 4, BIG), st.ST_EINVAL),              # n1 < 1
+    ((P, 12, 1152, P2, 1152, st.ST_BF16, 3, -1, BIG), st.ST_EINVAL),             # n2 < 1
+    ((P, 10, 1152, P2, 1152, st.ST_BF16, 3, 4, BIG), st.ST_EINVAL),              # rows not a multiple of n1*n2
+    ((P, -12, 1152, P2, 1152, st.ST_BF16, 3, 4, BIG), st.ST_EINVAL),
+    ((None, 12, 1152, P2, 1152, st.ST_BF16, 3, 4, BIG), st.ST_EINVAL),
+    ((P, 12, 1152, P2, 1150, st.ST_BF16, 3, 4, BIG), st.ST_EUNSUPPORTED),        # n_out % 4
+    ((P, 12, 1160, P2, 1152, st.ST_BF16, 3, 4, BIG), st.ST_EUNSUPPORTED),        # bf16 k_in % 64
+    ((P, 12, 1152, P2, 1152, 3, 3, 4, BIG), st.ST_EINVAL),                       # dtype
+    ((P, 12, 1152, P2, 1152, st.ST_BF16, 3, 4, P + 16), st.ST_EINVAL),          # y overlaps a
+    ((P, 12, 1152, P2, 1152, st.ST_BF16, 3, 4, BIG + 2), st.ST_EALIGN),
+])
+def test_out_proj_relayout_validation(args, want):
+    assert code(st.st_out_proj_relayout, *args) == want
+
+
+@pytest.mark.parametrize("args,want", [
     ((None, P2, P3, 1, 51, 8160, 16, 72, 0.1, st.ST_BF16, BIG), st.ST_EINVAL),
     ((P, P2, P3, 1, 51, 8160, 16, 72, 0.0, st.ST_BF16, BIG), st.ST_EINVAL),       # scale must be > 0
     ((P, P2, P3, 1, 51, 8160, 16, 72, float("nan"), st.ST_BF16, BIG), st.ST_EINVAL),

@@ -66,7 +66,7 @@ def check_layer_pair_stepwise(lp, x_dev, wh, grid_w, sample_rows=None, attn_chec
     """Run lp's steps one at a time; check each against the oracle on the GPU's own inputs."""
     B, T, S, C, H, d = lp.B, lp.T, lp.S, lp.C, lp.H, lp.d
     bf = lp.dtype == st.ST_BF16
-    steps = dict(lp.steps(x_dev))
+    steps = dict(lp.steps(x_dev, fused=False))   # separate relayout passes, each checked
     rows = np.arange(lp.N) if sample_rows is None else sample_rows
     rows_d = t_.as_tensor(rows, device="cuda")
     sel = lambda t: f64(t.reshape(lp.N, -1).index_select(0, rows_d))   # noqa: E731  gather on the device first
@@ -131,7 +131,11 @@ def test_layer_pair_bf16_stepwise_and_end_to_end(T, S, grid_w, C, H, d):
     check_layer_pair_stepwise(lp, xd, wh, grid_w)
     y_ref = oracle.block(f64(x), wh["s"], wh["t"], H, d, grid_w, EPS, BASE)
     assert_close(f64(lp.y).reshape(y_ref.shape), y_ref, True, "block end to end")
-    # the native orchestration runs the same launches: bit-identical
+    # relayouts fused into the output projections' stores: bit-identical
+    y_sep = lp.y.clone()
+    lp.run(xd, fused=True)
+    assert t_.equal(lp.y, y_sep)
+    # the native orchestration runs the same arithmetic: bit-identical
     yb = run_block(xd, wd, T, T, S, grid_w, C, H, d, 1, 1, st.ST_BF16)
     assert t_.equal(yb.view(-1), lp.y.view(-1))
 
@@ -178,6 +182,9 @@ def test_tiny_fp32_workload_block():
     check_layer_pair_stepwise(lp, xd, wh, grid_w)
     y_ref = oracle.block(f64(inp["x"]), wh["s"], wh["t"], H, d, grid_w, EPS, BASE)
     assert_close(f64(lp.y).reshape(y_ref.shape), y_ref, False, "fp32 block")
+    y_sep = lp.y.clone()
+    lp.run(xd, fused=True)
+    assert t_.equal(lp.y, y_sep)
     y1 = run_block(xd, wd, T, T, S, grid_w, C, H, d, 1, 1, st.ST_F32)
     y2 = run_block(xd, wd, T, T, S, grid_w, C, H, d, 2, 2, st.ST_F32)
     assert t_.equal(y1.view(-1), lp.y.view(-1))
@@ -211,7 +218,9 @@ def test_720p_full_size_sampled():
 def test_1080p_full_size_sampled_and_sliced_schedule():
     lp, xd, wd, res, (T, S, grid_w, C, H, d) = full_size(3, attn_pairs=[(0, 0), (50, 15)])
     print({k: (round(a, 5), round(r, 5)) for k, (a, r) in res.items()})
-    y3 = lp.y.view(1, T, S, C)
+    y3 = lp.y.view(1, T, S, C).clone()
+    lp.run(xd, fused=True)   # the bench's launch sequence: relayouts fused into the projections
+    assert t_.equal(lp.y.view(1, T, S, C), y3)
     yb = run_block(xd, wd, T, T, S, grid_w, C, H, d, 1, 1, st.ST_BF16)
     assert t_.equal(yb, y3)
     del lp, yb

@@ -202,6 +202,29 @@ def test_out_proj(rows, K, N, dt):
     assert_close(f64(y), oracle.linear(f64(a), f64(w)), bf16=dt == BF, what="y")
 
 
+# rows in [outer, n1, n2] order stored as [outer, n2, n1]: ragged GEMM tiles (rows not a
+# multiple of 256), the 288-channel and the 256-channel tilings, fp32
+@pytest.mark.parametrize("outer,n1,n2,K,N,dt", [(2, 5, 37, 1152, 1152, BF), (1, 51, 13, 384, 384, BF),
+                                                (3, 7, 9, 1152, 100, BF), (1, 4, 6, 128, 128, F32),
+                                                (1, 1, 70, 128, 64, BF)])
+def test_out_proj_relayout(outer, n1, n2, K, N, dt):
+    sd = "bf16" if dt == BF else "f32"
+    rows = outer * n1 * n2
+    a = st_synth.randn((rows, K), 31 + rows, dtype=sd)
+    w = st_synth.randn((N, K), 32 + rows, std=0.02, dtype=sd)
+    ad, wd = to_dev(a), to_dev(w)
+    y, y_ref = empty((rows, N), dt == BF), empty((rows, N), dt == BF)
+    h = empty((rows, N), dt == BF)
+    st.st_out_proj_relayout(ad, rows, K, wd, N, dt, n1, n2, y)
+    st.st_out_proj(ad, rows, K, wd, N, dt, h)
+    eb = 2 if dt == BF else 4
+    st.st_relayout(h, [n1 * n2 * N, n2 * N, N, 1], y_ref, [n1 * n2 * N, N, n1 * N, 1], [outer, n1, n2, N], 4, eb)
+    sync()
+    assert t_.equal(y, y_ref)   # the fused store is bit-identical to projection + relayout
+    ref = oracle.bt_to_bs(oracle.linear(f64(a), f64(w)).reshape(outer, n1, n2, N)).reshape(rows, N)
+    assert_close(f64(y), ref, bf16=dt == BF, what="y")
+
+
 # --------------------------------------------------------------------------- #
 # Attention                                                                    #
 # --------------------------------------------------------------------------- #
