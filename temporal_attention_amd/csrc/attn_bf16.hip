@@ -28,8 +28,9 @@
 // units), so exponentials stay <= 2^8 in between.
 // Short sequences (attn_short_kernel, L <= 64): one wave per (outer, head)
 // loads its whole Q and K straight into operand registers and V^T through a
-// private LDS slice; a workgroup covers all heads of one outer index, which
-// is one contiguous [L, H, d] block of each tensor.
+// private LDS slice; a workgroup covers four adjacent heads of one outer
+// index, so its loads share cache lines, and every wave has exactly one head
+// to do, so all of them are in flight at once.
 #include <math.h>
 
 #include "st_internal.h"
@@ -648,12 +649,15 @@ struct ShortCfg {
 };
 
 template <int D, int NT>
-__global__ void __launch_bounds__(256, 2) attn_short_kernel(AttnArgs a, uint32_t nblocks) {
+__global__ void __launch_bounds__(256) attn_short_kernel(AttnArgs a, uint32_t nblocks) {
   typedef ShortCfg<D, NT> C;
   typedef Dims<D> DM;
   __shared__ __attribute__((aligned(16))) u16 lds[4 * C::V_WAVE];
 
-  const int64_t outer = xcd_remap(blockIdx.x, nblocks);
+  const uint32_t hg_n = (uint32_t)(a.H + 3) / 4;
+  const uint32_t blk = xcd_remap(blockIdx.x, nblocks);
+  const int64_t outer = blk / hg_n;
+  const int h0 = (int)(blk % hg_n) * 4, h1 = min(a.H, h0 + 4);
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int l32 = lane & 31, g = lane >> 5;
@@ -667,7 +671,7 @@ __global__ void __launch_bounds__(256, 2) attn_short_kernel(AttnArgs a, uint32_t
     Vs[dd * C::V_LD + i % C::V_LD] = (DM::ONES && dd == D) ? (u16)0x3F80 : (u16)0;
   }
 
-  for (int h = wave; h < a.H; h += 4) {
+  for (int h = h0 + wave; h < h1; h += 4) {
     const int64_t base = outer * L * rs + (int64_t)h * D;
     const u16 *qp = a.q + base, *kp = a.k + base, *vp = a.v + base;
     u16 *op = a.o + base;
@@ -822,8 +826,9 @@ st_status launch_long(const AttnArgs &a, hipStream_t s) {
 
 template <int D, int NT>
 st_status launch_short(const AttnArgs &a, hipStream_t s) {
-  if (a.outer >= (1ll << 31)) return ST_EUNSUPPORTED;
-  hipLaunchKernelGGL((attn_short_kernel<D, NT>), dim3((uint32_t)a.outer), dim3(256), 0, s, a, (uint32_t)a.outer);
+  const int64_t nb = a.outer * ((a.H + 3) / 4);
+  if (nb >= (1ll << 31)) return ST_EUNSUPPORTED;
+  hipLaunchKernelGGL((attn_short_kernel<D, NT>), dim3((uint32_t)nb), dim3(256), 0, s, a, (uint32_t)nb);
   return launch_status();
 }
 

@@ -266,6 +266,7 @@ TEMPORAL_CASES = [
     (1, 3, 80, 70, 2, 72, BF),         # longer than the short kernel: long path
     (1, 9, 1, 1, 2, 72, BF),           # T = 1
     (1, 7, 33, 33, 2, 64, BF),
+    (2, 5, 40, 37, 6, 64, BF),         # two head groups per (b, s), the second one partial
     (1, 4, 20, 20, 2, 128, BF),        # d = 128: long path
     (1, 64, 4, 4, 2, 64, F32),
     (1, 6, 10, 7, 2, 64, F32),
