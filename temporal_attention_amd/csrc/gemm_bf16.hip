@@ -143,9 +143,16 @@ __device__ __forceinline__ void gemm_step(const u16 *__restrict__ As, const u16 
   }
 }
 
-template <int CT, int D>
+template <int CT, int D, typename TabPtr>
 __device__ __forceinline__ void epilogue_qkv(const GemmArgs &a, f32x4 (&acc)[CT][kTT], int64_t m0, int nw0, int wm,
-                                             int l16, int g4);
+                                             int l16, int g4, TabPtr tab);
+
+// Floats of the RoPE table (npos positions x pairs x {cos, sin}); 0 without RoPE.
+template <int D>
+__device__ __forceinline__ int64_t rope_table_floats(const RopeArgs &r) {
+  if (r.kind == ST_ROPE_NONE) return 0;
+  return (int64_t)r.npos * (r.kind == ST_ROPE_2D ? D / 4 : D / 2) * 2;
+}
 
 // MODE 0: plain output y.  MODE 1: q/k/v with RMSNorm + RoPE on q, k (head dim D).
 template <int CT, int MODE, int D>
@@ -180,12 +187,28 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_bf16_kernel(GemmArgs a, uint
   dma.init(a, m0, n0, lane, wave);
   const u16 *xb = a.x + m0 * a.K;
   const int nk = a.K / kBK;
+  // MODE 1: the RoPE table moves into the stage the last K step leaves free
+  // (its loads overlap that step's MFMAs), so the epilogue's cos/sin reads are
+  // LDS reads instead of dependent global loads.  Tables larger than a stage
+  // are read from global memory.
+  int64_t tab_floats = 0;
+  if constexpr (MODE == 1) tab_floats = rope_table_floats<D>(a.rope);
+  const bool tab_lds = tab_floats > 0 && tab_floats * 4 <= TL::STAGE * 2;
   dma.issue(lds, 0, xb, a.w, wave);
   wait_vmem_upto<0>();
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     u16 *cur = lds + (kt & 1) * TL::STAGE;
     u16 *nxt = lds + ((kt & 1) ^ 1) * TL::STAGE;
+    if (kt + 1 == nk && tab_lds) {
+      // 1 KB per wave instruction; the last block's lanes past the end re-read the last 16 bytes
+      const int blocks = (int)((tab_floats + 255) / 256);
+      for (int b = wave; b < blocks; b += TL::NWAVES) {
+        const int64_t f = min<int64_t>((int64_t)b * 256 + lane * 4, tab_floats - 4);
+        __builtin_amdgcn_global_load_lds(a.rope.table + f, (__attribute__((address_space(3))) void *)(nxt + b * 512),
+                                         16, 0, 0);
+      }
+    }
     gemm_step<CT>(cur, cur + TL::LDS_A, nxt, kt + 1 < nk, (kt + 1) * kBK, dma, xb, a.w, wave, wn, wm, l16, g4, acc);
     wait_vmem_upto<0>();
     __syncthreads();
@@ -210,14 +233,19 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_bf16_kernel(GemmArgs a, uint
       }
     }
   } else {
-    epilogue_qkv<CT, D>(a, acc, m0, nw0, wm, l16, g4);
+    if (tab_lds) {
+      const float *t = reinterpret_cast<const float *>(lds + (nk & 1) * TL::STAGE);   // the last step's free stage
+      epilogue_qkv<CT, D>(a, acc, m0, nw0, wm, l16, g4, t);
+    } else {
+      epilogue_qkv<CT, D>(a, acc, m0, nw0, wm, l16, g4, a.rope.table);
+    }
   }
 }
 
 // MODE 1 epilogue: the wave's channels are HPW whole heads.
-template <int CT, int D>
+template <int CT, int D, typename TabPtr>
 __device__ __forceinline__ void epilogue_qkv(const GemmArgs &a, f32x4 (&acc)[CT][kTT], int64_t m0, int nw0, int wm,
-                                             int l16, int g4) {
+                                             int l16, int g4, TabPtr tab) {
   typedef Tile<CT> TL;
   constexpr int HPW = TL::WN / D;
   static_assert(TL::WN % D == 0, "wave channel range must hold whole heads");
@@ -225,6 +253,26 @@ __device__ __forceinline__ void epilogue_qkv(const GemmArgs &a, f32x4 (&acc)[CT]
   const int hd = H * D;
   const int gh0 = nw0 / D;   // global head index (over 3H) of the wave's first head
   const int npairs = a.rope.kind == ST_ROPE_2D ? D / 4 : D / 2;
+
+  // A wave whose heads are all v heads stores the projection as it is.
+  if (gh0 / H == 2 && (gh0 + HPW - 1) / H == 2) {
+#pragma unroll
+    for (int tt = 0; tt < kTT; ++tt) {
+      const int64_t r = m0 + wm * kWM + tt * 16 + l16;
+      if (r >= a.M) continue;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const int cl = ct * 16 + g4 * 4;
+        const int gh = gh0 + cl / D;
+        if (gh >= 3 * H) continue;
+        uint2 o;
+        o.x = pack_bf16x2(acc[ct][tt][0], acc[ct][tt][1]);
+        o.y = pack_bf16x2(acc[ct][tt][2], acc[ct][tt][3]);
+        *reinterpret_cast<uint2 *>(a.v + r * hd + (gh - 2 * H) * D + (cl - (cl / D) * D)) = o;
+      }
+    }
+    return;
+  }
 
   // Pass 1, per token row of the lane: 1 / RMS of each head of the wave, and
   // the token's RoPE position.  A lane's 4 channels of one MFMA tile belong to
@@ -295,7 +343,7 @@ __device__ __forceinline__ void epilogue_qkv(const GemmArgs &a, f32x4 (&acc)[CT]
                     acc[ct][tt][3] * invh * g.w};
       if (a.rope.kind != ST_ROPE_NONE) {
         const int pos = second ? p1[tt] : p0[tt];
-        const float4 cs = *reinterpret_cast<const float4 *>(a.rope.table + ((int64_t)pos * npairs + pair) * 2);
+        const float4 cs = *reinterpret_cast<const float4 *>(tab + ((int64_t)pos * npairs + pair) * 2);
         const float x0 = o[0], x1 = o[1], x2 = o[2], x3 = o[3];
         o[0] = x0 * cs.x - x1 * cs.y;
         o[1] = x0 * cs.y + x1 * cs.x;
