@@ -23,6 +23,8 @@
 // as large as the LDS allows and every load instruction covers whole lines.
 // The grid is remapped so the channel tiles of one token block run on the same
 // XCD and share its L2 copy of the activations.
+#include <type_traits>
+
 #include "st_internal.h"
 
 namespace st {
@@ -318,46 +320,55 @@ __device__ __forceinline__ void epilogue_qkv(const GemmArgs &a, f32x4 (&acc)[CT]
   }
 
   // Pass 2, channel tile outer: the tile's head, section (q, k, v), gains and
-  // rotation pair are fixed for all token rows.  v heads skip the arithmetic
-  // by select, so there is no divergent branch.
+  // rotation pair are fixed for all token rows.  GENERAL covers a wave with
+  // rows past the last one, channel tiles past the last head or v heads
+  // (by select, no divergent branch); every other wave takes the copy of the
+  // loop without those checks.
+  auto pass2 = [&](auto general) {
+    constexpr bool GENERAL = decltype(general)::value;
 #pragma unroll
-  for (int ct = 0; ct < CT; ++ct) {
-    const int cl = ct * 16 + g4 * 4;
-    const int hh = cl / D;
-    const int gh = gh0 + hh;
-    if (gh >= 3 * H) continue;
-    const int which = gh / H;              // 0 q, 1 k, 2 v
-    const int jd = cl - hh * D;            // dim within the head (multiple of 4)
-    const bool norm = which < 2;
-    const float4 g = *reinterpret_cast<const float4 *>((which == 0 ? a.g_q : a.g_k) + jd);
-    const bool second = a.rope.kind == ST_ROPE_2D && jd >= D / 2;
-    const int pair = (jd - (second ? D / 2 : 0)) >> 1;
-    u16 *dst = (which == 0 ? a.q : (which == 1 ? a.k : a.v)) + (gh - which * H) * D + jd;
+    for (int ct = 0; ct < CT; ++ct) {
+      const int cl = ct * 16 + g4 * 4;
+      const int hh = cl / D;
+      const int gh = gh0 + hh;
+      if (GENERAL && gh >= 3 * H) continue;
+      const int which = gh / H;              // 0 q, 1 k, 2 v
+      const int jd = cl - hh * D;            // dim within the head (multiple of 4)
+      const bool norm = !GENERAL || which < 2;
+      const float4 g = *reinterpret_cast<const float4 *>((which == 0 ? a.g_q : a.g_k) + jd);
+      const bool second = a.rope.kind == ST_ROPE_2D && jd >= D / 2;
+      const int pair = (jd - (second ? D / 2 : 0)) >> 1;
+      u16 *dst = (which == 0 ? a.q : (which == 1 ? a.k : a.v)) + (gh - which * H) * D + jd;
 #pragma unroll
-    for (int tt = 0; tt < kTT; ++tt) {
-      if (roff[tt] < 0) continue;
-      float invh = inv[tt][0];
+      for (int tt = 0; tt < kTT; ++tt) {
+        if (GENERAL && roff[tt] < 0) continue;
+        float invh = inv[tt][0];
 #pragma unroll
-      for (int h2 = 1; h2 < HPW; ++h2) invh = hh == h2 ? inv[tt][h2] : invh;
-      float o[4] = {acc[ct][tt][0] * invh * g.x, acc[ct][tt][1] * invh * g.y, acc[ct][tt][2] * invh * g.z,
-                    acc[ct][tt][3] * invh * g.w};
-      if (a.rope.kind != ST_ROPE_NONE) {
-        const int pos = second ? p1[tt] : p0[tt];
-        const float4 cs = *reinterpret_cast<const float4 *>(tab + ((int64_t)pos * npairs + pair) * 2);
-        const float x0 = o[0], x1 = o[1], x2 = o[2], x3 = o[3];
-        o[0] = x0 * cs.x - x1 * cs.y;
-        o[1] = x0 * cs.y + x1 * cs.x;
-        o[2] = x2 * cs.z - x3 * cs.w;
-        o[3] = x2 * cs.w + x3 * cs.z;
+        for (int h2 = 1; h2 < HPW; ++h2) invh = hh == h2 ? inv[tt][h2] : invh;
+        float o[4] = {acc[ct][tt][0] * invh * g.x, acc[ct][tt][1] * invh * g.y, acc[ct][tt][2] * invh * g.z,
+                      acc[ct][tt][3] * invh * g.w};
+        if (a.rope.kind != ST_ROPE_NONE) {
+          const int pos = second ? p1[tt] : p0[tt];
+          const float4 cs = *reinterpret_cast<const float4 *>(tab + ((int64_t)pos * npairs + pair) * 2);
+          const float x0 = o[0], x1 = o[1], x2 = o[2], x3 = o[3];
+          o[0] = x0 * cs.x - x1 * cs.y;
+          o[1] = x0 * cs.y + x1 * cs.x;
+          o[2] = x2 * cs.z - x3 * cs.w;
+          o[3] = x2 * cs.w + x3 * cs.z;
+        }
+        if (GENERAL)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o[j] = norm ? o[j] : acc[ct][tt][j];
+        uint2 ov;
+        ov.x = pack_bf16x2(o[0], o[1]);
+        ov.y = pack_bf16x2(o[2], o[3]);
+        *reinterpret_cast<uint2 *>(dst + roff[tt]) = ov;
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) o[j] = norm ? o[j] : acc[ct][tt][j];
-      uint2 ov;
-      ov.x = pack_bf16x2(o[0], o[1]);
-      ov.y = pack_bf16x2(o[2], o[3]);
-      *reinterpret_cast<uint2 *>(dst + roff[tt]) = ov;
     }
-  }
+  };
+  const bool full_rows = m0 + kBM <= a.M;       // whole workgroup
+  if (full_rows && gh0 + HPW <= 2 * H) pass2(std::false_type{});   // q and k heads only, every row present
+  else pass2(std::true_type{});
 }
 
 template <int CT, int MODE, int D>
