@@ -257,7 +257,8 @@ def time_a2a_local(B, T, S, C, P, reps, stream):
 def time_chunked_attention(lp, B, T, S, H, d, reps, stream, n_chunks=4):
     """Spatial attention of the step's q, k, v as a 4-way key split, the work of one GPU of a
     4-way ring: st_attn_chunk per key chunk (with log-sum-exp), folded together by three
-    in-place st_attn_merge calls; against one st_attn_chunk over all keys."""
+    in-place st_attn_merge calls, and the same with the merges inside the attention epilogue
+    (st_attn_chunk_acc); against one st_attn_chunk over all keys."""
     import torch
 
     import temporal_attention_amd as st
@@ -284,7 +285,12 @@ def time_chunked_attention(lp, B, T, S, H, d, reps, stream, n_chunks=4):
     def merge_only():
         st.st_attn_merge(acc, lse_acc, part, lse_part, outer, S, H, d, st.ST_BF16, acc, lse_acc)
 
-    for name, fn in (("whole", whole), ("chunked", chunked), ("merge", merge_only)):
+    def fused():   # first chunk fresh, later chunks merged in the attention epilogue
+        for i, (a, b) in enumerate(zip(bounds, bounds[1:])):
+            fn = st.st_attn_chunk if i == 0 else st.st_attn_chunk_acc
+            fn(lp.q, kc[i], vc[i], outer, S, b - a, b - a, H, d, scale, st.ST_BF16, acc, lse_acc)
+
+    for name, fn in (("whole", whole), ("chunked", chunked), ("merge", merge_only), ("fused", fused)):
         fn()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -298,6 +304,8 @@ def time_chunked_attention(lp, B, T, S, H, d, reps, stream, n_chunks=4):
     merge_bytes = outer * S * H * (3 * d * 2 + 3 * 4)     # read two rows + lse, write one row + lse
     return {"n_chunks": n_chunks, "ms": round(times["chunked"], 4), "unchunked_with_lse_ms": round(times["whole"], 4),
             "overhead": round(times["chunked"] / times["whole"] - 1.0, 4),
+            "fused_merge_ms": round(times["fused"], 4),
+            "fused_merge_overhead": round(times["fused"] / times["whole"] - 1.0, 4),
             "tflops": round(fl / times["chunked"] / 1e9, 1), "merge_ms": round(times["merge"], 4),
             "merge_gbs": round(merge_bytes / times["merge"] / 1e6, 1),
             "merge_frac_hbm_peak": round(merge_bytes / times["merge"] / 1e6 / PEAK_HBM_GBS, 4)}

@@ -193,6 +193,29 @@ st_status st_attn_chunk(const void *q, const void *k, const void *v, int64_t out
                         int H, int d, float scale, int dtype, void *out, float *lse, void *stream);
 
 /*
+ * st_attn_chunk_acc -- st_attn_chunk and st_attn_merge in one pass: the step
+ * Ring and Torus attention repeat as each key/value chunk arrives (same
+ * passages as st_attn_chunk).  acc_o / acc_lse hold the result over the keys
+ * seen so far and receive the result over those keys and this chunk:
+ *   lse_c = log sum_j exp(scale * q_i . k_j)          over this chunk's keys
+ *   acc_lse' = log(exp(acc_lse) + exp(lse_c))
+ *   acc_o'   = exp(acc_lse - acc_lse') acc_o + exp(lse_c - acc_lse') softmax_j(..) v_j
+ * The chunk's own output never leaves the kernel (fp32 in registers), so the
+ * merge costs one read of the accumulator instead of a separate pass over two
+ * partial results.  acc_lse = -inf marks an empty accumulator: its acc_o row
+ * is then ignored (any contents) and the call writes this chunk's result,
+ * bit-identical to st_attn_chunk.  kv_valid = 0 leaves the accumulator as it is.
+ *
+ *   q, k, v, kv_valid   as st_attn_chunk
+ *   acc_o     in/out  [outer, Lq, H, d]   (dtype)
+ *   acc_lse   in/out  fp32 [outer, H, Lq], 4-byte aligned
+ * Same validation and error codes as st_attn_chunk (acc_o, acc_lse in the
+ * roles of out, lse).
+ */
+st_status st_attn_chunk_acc(const void *q, const void *k, const void *v, int64_t outer, int Lq, int Lk, int kv_valid,
+                            int H, int d, float scale, int dtype, void *acc_o, float *acc_lse, void *stream);
+
+/*
  * st_attn_merge -- the attention result over the union of two disjoint key
  * chunks, from the two chunk results (st_attn_chunk or earlier merges):
  *   lse = log(exp(lse_a) + exp(lse_b)),

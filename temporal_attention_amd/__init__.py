@@ -6,7 +6,7 @@ meaning, layout and error behaviour of every entry point.
 """
 from ._lib import (  # noqa: F401
     EXPORTS, LIB_PATH, ST_BF16, ST_EALIGN, ST_EINVAL, ST_ELAUNCH, ST_EUNSUPPORTED, ST_EWORKSPACE, ST_F32, ST_OK,
-    ST_ROPE_1D, ST_ROPE_2D, ST_ROPE_NONE, STError, layer_weights, lib, st_attn_chunk, st_attn_merge,
+    ST_ROPE_1D, ST_ROPE_2D, ST_ROPE_NONE, STError, layer_weights, lib, st_attn_chunk, st_attn_chunk_acc, st_attn_merge,
     st_attn_spatial, st_attn_temporal,
     st_block_sliced, st_block_sliced_2s, st_block_sliced_workspace, st_v_change, st_layer_weights, st_out_proj,
     st_out_proj_relayout, st_qkv_norm_rope, st_relayout,

@@ -23,8 +23,9 @@ ST_ROPE_NONE, ST_ROPE_1D, ST_ROPE_2D = 0, 1, 2
 # Every entry point declared in include/st.h.
 EXPORTS = (
     "st_status_str", "st_rope_table_floats", "st_rope_table", "st_qkv_norm_rope", "st_out_proj",
-    "st_out_proj_relayout", "st_attn_spatial", "st_attn_temporal", "st_attn_chunk", "st_attn_merge", "st_relayout",
-    "st_block_sliced", "st_block_sliced_2s", "st_block_sliced_workspace", "st_v_change",
+    "st_out_proj_relayout", "st_attn_spatial", "st_attn_temporal", "st_attn_chunk", "st_attn_chunk_acc",
+    "st_attn_merge", "st_relayout", "st_block_sliced", "st_block_sliced_2s", "st_block_sliced_workspace",
+    "st_v_change",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -63,6 +64,7 @@ _SIGS = {
     "st_attn_spatial": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p, _p]),
     "st_attn_temporal": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p, _p]),
     "st_attn_chunk": (_i, [_p, _p, _p, _i64, _i, _i, _i, _i, _i, _f, _i, _p, _p, _p]),
+    "st_attn_chunk_acc": (_i, [_p, _p, _p, _i64, _i, _i, _i, _i, _i, _f, _i, _p, _p, _p]),
     "st_attn_merge": (_i, [_p, _p, _p, _p, _i64, _i, _i, _i, _i, _p, _p, _p]),
     "st_v_change": (_i, [_p, _p, _i64, _i, _i, _f, _i, _p, _p, _p, _i, _p]),
     "st_relayout": (_i, [_p, C.POINTER(C.c_int64), _p, C.POINTER(C.c_int64), C.POINTER(C.c_int64), _i, _i, _p]),
@@ -146,6 +148,11 @@ def st_attn_temporal(q, k, v, B, S, T, t_valid, H, d, scale, dtype, out, stream=
 def st_attn_chunk(q, k, v, outer, Lq, Lk, kv_valid, H, d, scale, dtype, out, lse, stream=None):
     _check("st_attn_chunk", lib.st_attn_chunk(_ptr(q), _ptr(k), _ptr(v), outer, Lq, Lk, kv_valid, H, d, scale, dtype,
                                               _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def st_attn_chunk_acc(q, k, v, outer, Lq, Lk, kv_valid, H, d, scale, dtype, acc_o, acc_lse, stream=None):
+    _check("st_attn_chunk_acc", lib.st_attn_chunk_acc(_ptr(q), _ptr(k), _ptr(v), outer, Lq, Lk, kv_valid, H, d, scale,
+                                                      dtype, _ptr(acc_o), _ptr(acc_lse), _stream(stream)))
 
 
 def st_attn_merge(o_a, lse_a, o_b, lse_b, outer, L, H, d, dtype, out, lse, stream=None):

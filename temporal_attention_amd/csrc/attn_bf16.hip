@@ -42,6 +42,7 @@ struct AttnArgs {
   const u16 *q, *k, *v;
   u16 *o;
   float *lse;          // optional [outer, H, L]: natural log-sum-exp of the scaled scores per query
+  int acc;             // o and lse hold a partial result over other keys: merge this one into it, in place
   int64_t outer;
   int L, Lk, n_valid, H;   // L queries, Lk keys per sequence (equal except for chunk attention)
   float c;             // scale * log2(e)
@@ -593,13 +594,27 @@ __global__ void __launch_bounds__(64 * kLongWaves, 8 / kLongWaves) attn_long_ker
     } else {
       l = w.lsum[nt] + __shfl_xor(w.lsum[nt], 32);
     }
-    const float inv = 1.0f / l;
     const int qi = q0 + nt * 32 + w.l32;
-    if (a.lse && qi < L && w.g == 0) {
+    // Output = fa * (accumulated row) + fp * (this result); without a.acc,
+    // fa = 0 and fp = 1.  The merge weights are exp(lse_part - lse_union).
+    float fa = 0.f, fp = 1.f;
+    if (a.lse) {
       // sum_j exp(scale s_j) = 2^M * l, M = the running max in scaled log2 units
       const float M = W::FOLD ? w.m[nt] : w.m[nt] * w.c;
-      a.lse[(outer * a.H + h) * (int64_t)L + qi] = (M + log2f(l)) * 0.69314718055994531f;
+      float lse = (M + log2f(l)) * 0.69314718055994531f;
+      const int64_t li = (outer * a.H + h) * (int64_t)L + qi;
+      if (a.acc) {
+        const float la = qi < L ? a.lse[li] : -INFINITY;   // read by both lane halves before g == 0 writes
+        const float mm = fmaxf(la, lse);
+        const float wa = expf(la - mm), wp = expf(lse - mm);
+        const float tot = wa + wp;
+        fa = wa / tot;
+        fp = wp / tot;
+        lse = mm + logf(tot);
+      }
+      if (qi < L && w.g == 0) a.lse[li] = lse;
     }
+    const float inv = fp / l;
     if (qi < L) {
       u16 *orow = op + (int64_t)qi * rs;
 #pragma unroll
@@ -608,26 +623,55 @@ __global__ void __launch_bounds__(64 * kLongWaves, 8 / kLongWaves) attn_long_ker
         for (int rb = 0; rb < 4; ++rb) {
           const int dd = dt * 32 + rb * 8 + w.g * 4;
           if (dd + 4 <= D) {
+            float x[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[j] = w.oacc[dt][nt][rb * 4 + j] * inv;
+            if (a.acc && fa > 0.f) {   // an empty accumulator contributes nothing, whatever its row holds
+              const uint2 pv = *reinterpret_cast<const uint2 *>(orow + dd);
+              x[0] = fmaf(fa, __uint_as_float(pv.x << 16), x[0]);
+              x[1] = fmaf(fa, __uint_as_float(pv.x & 0xFFFF0000u), x[1]);
+              x[2] = fmaf(fa, __uint_as_float(pv.y << 16), x[2]);
+              x[3] = fmaf(fa, __uint_as_float(pv.y & 0xFFFF0000u), x[3]);
+            }
             uint2 o;
-            o.x = pack_bf16x2(w.oacc[dt][nt][rb * 4 + 0] * inv, w.oacc[dt][nt][rb * 4 + 1] * inv);
-            o.y = pack_bf16x2(w.oacc[dt][nt][rb * 4 + 2] * inv, w.oacc[dt][nt][rb * 4 + 3] * inv);
+            o.x = pack_bf16x2(x[0], x[1]);
+            o.y = pack_bf16x2(x[2], x[3]);
             *reinterpret_cast<uint2 *>(orow + dd) = o;
           }
         }
     }
     if constexpr (DM::PV16) {
       // 16x16 accumulator: lane l holds rows 4 (l / 16) .. +3 for query (l & 15) of each half
+      // merge weights of query (lane & 15) + 16 h live in the lane of the 32x32 layout that holds it
+      float fa16[2], fp16[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        fa16[h] = __shfl(fa, h * 16 + (lane & 15));
+        fp16[h] = __shfl(fp, h * 16 + (lane & 15));
+      }
       const int dd = D - D % 32 + 4 * (lane >> 4);
       if (dd + 4 <= D) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int qh = q0 + nt * 32 + h * 16 + (lane & 15);
+          const float fah = fa16[h], fph = fp16[h];
           if (qh < L) {
-            const float ih = 1.0f / lh[h];
+            const float ih = fph / lh[h];
+            u16 *orow = op + (int64_t)qh * rs + dd;
+            float x[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[j] = w.oacc16[nt][h][j] * ih;
+            if (a.acc && fah > 0.f) {
+              const uint2 pv = *reinterpret_cast<const uint2 *>(orow);
+              x[0] = fmaf(fah, __uint_as_float(pv.x << 16), x[0]);
+              x[1] = fmaf(fah, __uint_as_float(pv.x & 0xFFFF0000u), x[1]);
+              x[2] = fmaf(fah, __uint_as_float(pv.y << 16), x[2]);
+              x[3] = fmaf(fah, __uint_as_float(pv.y & 0xFFFF0000u), x[3]);
+            }
             uint2 o;
-            o.x = pack_bf16x2(w.oacc16[nt][h][0] * ih, w.oacc16[nt][h][1] * ih);
-            o.y = pack_bf16x2(w.oacc16[nt][h][2] * ih, w.oacc16[nt][h][3] * ih);
-            *reinterpret_cast<uint2 *>(op + (int64_t)qh * rs + dd) = o;
+            o.x = pack_bf16x2(x[0], x[1]);
+            o.y = pack_bf16x2(x[2], x[3]);
+            *reinterpret_cast<uint2 *>(orow) = o;
           }
         }
       }
@@ -833,13 +877,14 @@ st_status launch_short(const AttnArgs &a, hipStream_t s) {
 }
 
 AttnArgs make_args(const void *q, const void *k, const void *v, int64_t outer, int L, int Lk, int n_valid, int H,
-                   float scale, void *out, float *lse) {
+                   float scale, void *out, float *lse, bool acc = false) {
   AttnArgs a;
   a.q = static_cast<const u16 *>(q);
   a.k = static_cast<const u16 *>(k);
   a.v = static_cast<const u16 *>(v);
   a.o = static_cast<u16 *>(out);
   a.lse = lse;
+  a.acc = acc ? 1 : 0;
   a.outer = outer;
   a.L = L;
   a.Lk = Lk;
@@ -860,9 +905,10 @@ st_status launch_attn_bf16(const void *q, const void *k, const void *v, int64_t 
 }
 
 st_status launch_attn_chunk_bf16(const void *q, const void *k, const void *v, int64_t outer, int Lq, int Lk,
-                                 int n_valid, int H, int d, float scale, void *out, float *lse, hipStream_t s) {
+                                 int n_valid, int H, int d, float scale, void *out, float *lse, hipStream_t s,
+                                 bool accumulate) {
   if (outer == 0 || Lq == 0) return ST_OK;
-  const AttnArgs a = make_args(q, k, v, outer, Lq, Lk, n_valid, H, scale, out, lse);
+  const AttnArgs a = make_args(q, k, v, outer, Lq, Lk, n_valid, H, scale, out, lse, accumulate);
   switch (d) {
     case 72: return launch_long<72, 2>(a, s);
     case 64: return launch_long<64, 2>(a, s);

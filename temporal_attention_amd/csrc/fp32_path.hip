@@ -80,8 +80,10 @@ __global__ void norm_rope_f32_kernel(int64_t rows, int H, int d, float *q, float
 // One thread per (outer, head, query): two passes over the keys.
 // One thread per (sequence, head, query); L queries over Lk keys, the first nv
 // of them valid (nv >= 1).  lse (optional, [outer, H, L]) gets m + log(l).
+// With acc, o and lse hold a partial result over other keys and receive its
+// merge with this one (weights exp(lse_part - lse_union)).
 __global__ void attn_f32_kernel(const float *q, const float *k, const float *v, int64_t outer, int L, int Lk, int nv,
-                                int H, int d, float scale, float *o, float *lse) {
+                                int H, int d, float scale, float *o, float *lse, int acc_mode) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= outer * H * L) return;
   const int qi = (int)(i % L);
@@ -112,8 +114,18 @@ __global__ void attn_f32_kernel(const float *q, const float *k, const float *v, 
     for (int c = 0; c < d; ++c) acc[c] = fmaf(p, vr[c], acc[c]);
   }
   float *orow = o + base + qi * rs;
+  const float lp = m + logf(l);
+  if (acc_mode) {
+    const float la = lse[oh * L + qi];
+    const float mm = fmaxf(la, lp);
+    const float wa = expf(la - mm), wp = expf(lp - mm), tot = wa + wp;
+    const float fa = wa / tot, fp = wp / tot;
+    for (int c = 0; c < d; ++c) orow[c] = (fa > 0.f ? fa * orow[c] : 0.f) + fp * (acc[c] / l);
+    lse[oh * L + qi] = mm + logf(tot);
+    return;
+  }
   for (int c = 0; c < d; ++c) orow[c] = acc[c] / l;
-  if (lse) lse[oh * L + qi] = m + logf(l);
+  if (lse) lse[oh * L + qi] = lp;
 }
 
 inline unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
@@ -147,17 +159,18 @@ st_status launch_attn_f32(const float *q, const float *k, const float *v, int64_
   if (n == 0) return ST_OK;
   if (blocks_for(n) >= (1u << 31)) return ST_EUNSUPPORTED;
   hipLaunchKernelGGL(attn_f32_kernel, dim3(blocks_for(n)), dim3(256), 0, s, q, k, v, outer, L, L, min(n_valid, L), H,
-                     d, scale, out, (float *)nullptr);
+                     d, scale, out, (float *)nullptr, 0);
   return launch_status();
 }
 
 st_status launch_attn_chunk_f32(const float *q, const float *k, const float *v, int64_t outer, int Lq, int Lk,
-                                int n_valid, int H, int d, float scale, float *out, float *lse, hipStream_t s) {
+                                int n_valid, int H, int d, float scale, float *out, float *lse, hipStream_t s,
+                                bool accumulate) {
   const int64_t n = outer * H * Lq;
   if (n == 0) return ST_OK;
   if (blocks_for(n) >= (1u << 31)) return ST_EUNSUPPORTED;
   hipLaunchKernelGGL(attn_f32_kernel, dim3(blocks_for(n)), dim3(256), 0, s, q, k, v, outer, Lq, Lk,
-                     min(n_valid, Lk), H, d, scale, out, lse);
+                     min(n_valid, Lk), H, d, scale, out, lse, accumulate ? 1 : 0);
   return launch_status();
 }
 

@@ -413,8 +413,8 @@ st_status st_attn_temporal(const void *q, const void *k, const void *v, int B, i
   return attn_common(q, k, v, (int64_t)B * S, T, t_valid, H, d, scale, dtype, out, true, stream);
 }
 
-st_status st_attn_chunk(const void *q, const void *k, const void *v, int64_t outer, int Lq, int Lk, int kv_valid,
-                        int H, int d, float scale, int dtype, void *out, float *lse, void *stream) {
+static st_status chunk_check(const void *q, const void *k, const void *v, int64_t outer, int Lq, int Lk, int kv_valid,
+                             int H, int d, float scale, int dtype, void *out, float *lse) {
   if (!dtype_ok(dtype)) return ST_EINVAL;
   if (!q || !k || !v || !out || !lse || H < 1 || outer < 0 || Lq < 0 || Lk < 0) return ST_EINVAL;
   if (kv_valid < 0 || kv_valid > Lk || d < 2 || d % 2) return ST_EINVAL;
@@ -430,13 +430,33 @@ st_status st_attn_chunk(const void *q, const void *k, const void *v, int64_t out
   for (const Range &in : {rq, rk, rv})
     if (overlap(ro, in) || overlap(rl, in)) return ST_EINVAL;
   if (overlap(ro, rl)) return ST_EINVAL;
+  return ST_OK;
+}
+
+st_status st_attn_chunk(const void *q, const void *k, const void *v, int64_t outer, int Lq, int Lk, int kv_valid,
+                        int H, int d, float scale, int dtype, void *out, float *lse, void *stream) {
+  const st_status c = chunk_check(q, k, v, outer, Lq, Lk, kv_valid, H, d, scale, dtype, out, lse);
+  if (c != ST_OK) return c;
   if (outer == 0 || Lq == 0) return ST_OK;
   hipStream_t s = (hipStream_t)stream;
-  if (kv_valid == 0) return launch_attn_empty(out, lse, outer, Lq, H, d, (int)e, s);
+  const int e = (int)esize(dtype);
+  if (kv_valid == 0) return launch_attn_empty(out, lse, outer, Lq, H, d, e, s);
   if (dtype == ST_F32)
     return launch_attn_chunk_f32((const float *)q, (const float *)k, (const float *)v, outer, Lq, Lk, kv_valid, H, d,
                                  scale, (float *)out, lse, s);
   return launch_attn_chunk_bf16(q, k, v, outer, Lq, Lk, kv_valid, H, d, scale, out, lse, s);
+}
+
+st_status st_attn_chunk_acc(const void *q, const void *k, const void *v, int64_t outer, int Lq, int Lk, int kv_valid,
+                            int H, int d, float scale, int dtype, void *acc_o, float *acc_lse, void *stream) {
+  const st_status c = chunk_check(q, k, v, outer, Lq, Lk, kv_valid, H, d, scale, dtype, acc_o, acc_lse);
+  if (c != ST_OK) return c;
+  if (outer == 0 || Lq == 0 || kv_valid == 0) return ST_OK;   // an empty chunk leaves the accumulator as it is
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == ST_F32)
+    return launch_attn_chunk_f32((const float *)q, (const float *)k, (const float *)v, outer, Lq, Lk, kv_valid, H, d,
+                                 scale, (float *)acc_o, acc_lse, s, true);
+  return launch_attn_chunk_bf16(q, k, v, outer, Lq, Lk, kv_valid, H, d, scale, acc_o, acc_lse, s, true);
 }
 
 st_status st_attn_merge(const void *o_a, const float *lse_a, const void *o_b, const float *lse_b, int64_t outer, int L,

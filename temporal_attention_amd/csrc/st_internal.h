@@ -91,11 +91,15 @@ st_status launch_attn_short_bf16(const void *q, const void *k, const void *v, in
 st_status launch_attn_f32(const float *q, const float *k, const float *v, int64_t outer, int L, int n_valid,
                           int H, int d, float scale, float *out, hipStream_t s);
 // Attention of Lq queries over a chunk of Lk keys (keys j >= n_valid masked, n_valid >= 1), optionally
-// writing the natural log-sum-exp of the scaled scores per query to lse [outer, H, Lq].
+// writing the natural log-sum-exp of the scaled scores per query to lse [outer, H, Lq].  With
+// accumulate, out and lse hold a partial result over other keys (lse -inf: none) and receive the
+// merge of it with this chunk's result.
 st_status launch_attn_chunk_bf16(const void *q, const void *k, const void *v, int64_t outer, int Lq, int Lk,
-                                 int n_valid, int H, int d, float scale, void *out, float *lse, hipStream_t s);
+                                 int n_valid, int H, int d, float scale, void *out, float *lse, hipStream_t s,
+                                 bool accumulate = false);
 st_status launch_attn_chunk_f32(const float *q, const float *k, const float *v, int64_t outer, int Lq, int Lk,
-                                int n_valid, int H, int d, float scale, float *out, float *lse, hipStream_t s);
+                                int n_valid, int H, int d, float scale, float *out, float *lse, hipStream_t s,
+                                bool accumulate = false);
 // o = 0 and lse = -inf for a chunk without valid keys; elem_bytes 2 or 4.
 st_status launch_attn_empty(void *o, float *lse, int64_t outer, int L, int H, int d, int elem_bytes, hipStream_t s);
 // Merge of two chunk results over [outer, L, H, d] with [outer, H, L] log-sum-exps (in place allowed).

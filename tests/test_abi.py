@@ -162,6 +162,8 @@ def chunk_args(**kw):
 ])
 def test_attn_chunk_validation(kw, want):
     assert code(st.st_attn_chunk, *chunk_args(**kw)) == want
+    # the accumulating form validates the same way (acc_o, acc_lse in the roles of out, lse)
+    assert code(st.st_attn_chunk_acc, *chunk_args(**kw)) == want
 
 
 def merge_args(**kw):

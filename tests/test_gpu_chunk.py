@@ -177,3 +177,87 @@ def test_chunked_merge_at_1080p_frame_shape_sampled():
         ro, rl = oracle.attention_lse(qf[0, rows, h], kf[0, :, h], vf[0, :, h], scale)
         assert_close(got_o[0, rows, h], ro, what=f"head {h}")
         assert np.max(np.abs(got_l[0, h, rows] - rl)) <= lse_tol(rl, BF)
+
+
+# --------------------------------------------------------------------------- #
+# st_attn_chunk_acc: chunk attention merged into a running accumulator        #
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("dt,d,Lq,Lk,kv_valid", [(BF, 72, 300, 500, 480), (BF, 64, 70, 200, 150), (BF, 128, 100, 130, 130),
+                                                 (F32, 64, 33, 40, 35)])
+def test_chunk_acc_into_empty_accumulator_is_chunk(dt, d, Lq, Lk, kv_valid):
+    # lse = -inf marks an empty accumulator: its rows are ignored, whatever they hold (NaN here)
+    outer, H = 2, 2
+    q, k, v = (to_dev(a) for a in tensors((outer, Lq, H, d), (outer, Lk, H, d), 1900 + d, dt))
+    scale = 1.0 / math.sqrt(d)
+    ref_o, ref_l = empty((outer, Lq, H, d), dt == BF), lse_buf(outer, H, Lq)
+    st.st_attn_chunk(q, k, v, outer, Lq, Lk, kv_valid, H, d, scale, dt, ref_o, ref_l)
+    acc_o = t_.full((outer, Lq, H, d), float("nan"), dtype=ref_o.dtype, device="cuda")
+    acc_l = t_.full((outer, H, Lq), -float("inf"), dtype=t_.float32, device="cuda")
+    st.st_attn_chunk_acc(q, k, v, outer, Lq, Lk, kv_valid, H, d, scale, dt, acc_o, acc_l)
+    sync()
+    assert t_.equal(acc_o, ref_o) and t_.equal(acc_l, ref_l)
+
+
+@pytest.mark.parametrize("dt,d,cuts,valid", [
+    (BF, 72, (300, 301), 950),        # three chunks, one of a single key, masked tail
+    (BF, 128, (64, 500), 700),
+    (BF, 64, (1,), 1000),
+    (F32, 64, (100, 450), 999),
+])
+def test_chunk_acc_running_equals_unchunked(dt, d, cuts, valid):
+    outer, L, H = 2, 1000, 2
+    q, k, v = tensors((outer, L, H, d), (outer, L, H, d), 2000 + d + len(cuts), dt, 2.0)
+    scale = 1.0 / math.sqrt(d)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    bounds = [0, *cuts, L]
+    acc_o = empty((outer, L, H, d), dt == BF)
+    acc_l = t_.full((outer, H, L), -float("inf"), dtype=t_.float32, device="cuda")
+    # the same chunks through st_attn_chunk + st_attn_merge, for comparison
+    m_o, m_l = empty((outer, L, H, d), dt == BF), lse_buf(outer, H, L)
+    p_o, p_l = empty((outer, L, H, d), dt == BF), lse_buf(outer, H, L)
+    for i, (a, b) in enumerate(zip(bounds, bounds[1:])):
+        kc, vc = kd[:, a:b].contiguous(), vd[:, a:b].contiguous()
+        nv = max(0, min(b, valid) - a)
+        st.st_attn_chunk_acc(qd, kc, vc, outer, L, b - a, nv, H, d, scale, dt, acc_o, acc_l)
+        dst_o, dst_l = (m_o, m_l) if i == 0 else (p_o, p_l)
+        st.st_attn_chunk(qd, kc, vc, outer, L, b - a, nv, H, d, scale, dt, dst_o, dst_l)
+        if i > 0:
+            st.st_attn_merge(m_o, m_l, p_o, p_l, outer, L, H, d, dt, m_o, m_l)
+    sync()
+    ro, rl = oracle.attn_chunk(f64(q), f64(k), f64(v), scale, valid)
+    assert_close(f64(acc_o), ro, bf16=dt == BF, what="accumulated O")
+    check_lse(acc_l, rl, dt, "accumulated lse")
+    # the fused merge rounds once per chunk where chunk + merge rounds twice: close, not identical
+    assert_close(f64(acc_o), f64(m_o), bf16=dt == BF, what="fused vs chunk + merge")
+
+
+def test_chunk_acc_empty_chunk_leaves_accumulator():
+    outer, L, H, d = 2, 50, 2, 72
+    q, k, v = (to_dev(a) for a in tensors((outer, L, H, d), (outer, 20, H, d), 2100, BF))
+    acc_o, acc_l = empty((outer, L, H, d)), lse_buf(outer, H, L)
+    st.st_attn_chunk(q, k, v, outer, L, 20, 20, H, d, 0.1, BF, acc_o, acc_l)
+    before_o, before_l = acc_o.clone(), acc_l.clone()
+    st.st_attn_chunk_acc(q, k, v, outer, L, 20, 0, H, d, 0.1, BF, acc_o, acc_l)   # kv_valid = 0
+    sync()
+    assert t_.equal(acc_o, before_o) and t_.equal(acc_l, before_l)
+
+
+def test_chunk_acc_1080p_frame_sampled():
+    # one 1080p frame in three uneven key chunks accumulated in place, checked on sampled queries
+    L, H, d, outer = 8160, 16, 72, 1
+    q, k, v = tensors((outer, L, H, d), (outer, L, H, d), 2200, BF)
+    scale = 1.0 / math.sqrt(d)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    acc_o = empty((outer, L, H, d))
+    acc_l = t_.full((outer, H, L), -float("inf"), dtype=t_.float32, device="cuda")
+    for a, b in zip([0, 3000, 3001], [3000, 3001, L]):
+        st.st_attn_chunk_acc(qd, kd[:, a:b].contiguous(), vd[:, a:b].contiguous(), outer, L, b - a, b - a, H, d, scale,
+                             BF, acc_o, acc_l)
+    sync()
+    rows = np.random.default_rng(2201).choice(L, 48, replace=False)
+    got_o, got_l = f64(acc_o), acc_l.cpu().numpy().astype(np.float64)
+    qf, kf, vf = f64(q), f64(k), f64(v)
+    for h in range(H):
+        ro, rl = oracle.attention_lse(qf[0, rows, h], kf[0, :, h], vf[0, :, h], scale)
+        assert_close(got_o[0, rows, h], ro, what=f"head {h}")
+        assert np.max(np.abs(got_l[0, h, rows] - rl)) <= lse_tol(rl, BF)
