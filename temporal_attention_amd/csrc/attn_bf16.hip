@@ -164,8 +164,8 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
 
 // K and V tiles go global -> LDS directly, 1 KB per wavefront instruction:
 // lane l of block b carries 16-byte chunk 64 b + l of the packed [key][d]
-// tile.  The 2 * BLOCKS blocks of a stage are dealt round-robin to the four
-// waves; each lane's element offset inside a tile (key * row stride + dim) is
+// tile.  The 2 * BLOCKS blocks of a stage are dealt round-robin to the
+// workgroup's waves; each lane's element offset inside a tile (key * row stride + dim) is
 // fixed for the whole key loop, so it is computed once.  Keys past L repeat
 // row L-1 (their scores are masked).
 template <int D>
