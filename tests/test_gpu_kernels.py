@@ -262,6 +262,9 @@ TEMPORAL_CASES = [
     (1, 37, 51, 51, 16, 72, BF),
     (1, 20, 52, 51, 16, 72, BF),
     (2, 10, 24, 24, 4, 72, BF),
+    (1, 11, 30, 27, 5, 72, BF),        # one query tile, masked keys, a partial head group
+    (1, 6, 32, 31, 4, 72, BF),         # one query tile, full
+    (1, 7, 17, 12, 3, 64, BF),
     (1, 5, 64, 60, 3, 72, BF),
     (1, 3, 80, 70, 2, 72, BF),         # longer than the short kernel: long path
     (1, 9, 1, 1, 2, 72, BF),           # T = 1
