@@ -27,10 +27,11 @@
 // accumulator when a query's running maximum grows by more than 8 (in log2
 // units), so exponentials stay <= 2^8 in between.
 // Short sequences (attn_short_kernel, L <= 64): one wave per (outer, head)
-// loads its whole Q and K straight into operand registers and V^T through a
-// private LDS slice; a workgroup covers four adjacent heads of one outer
-// index, so its loads share cache lines, and every wave has exactly one head
-// to do, so all of them are in flight at once.
+// loads its whole Q and K straight into operand registers and copies V
+// global -> LDS into a private slice, read back as V^T by transpose reads; a
+// workgroup covers four adjacent heads of one outer index, so its loads share
+// cache lines, and every wave has exactly one head to do, so all of them are
+// in flight at once.
 #include <math.h>
 
 #include "st_internal.h"
@@ -73,27 +74,6 @@ __device__ __forceinline__ uint4 tr_read_pair(const u16 *p) {
   const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(p + 8 * D));
   const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
   return make_uint4(a.x, a.y, b.x, b.y);
-}
-
-__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
-__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
-
-// Transpose 4 keys x 8 dims (4 x uint4) into 8 dims x 4 keys (8 x uint2).
-__device__ __forceinline__ void transpose4x8(const uint4 (&kv)[4], uint2 (&out)[8]) {
-  const uint32_t w[4][4] = {{kv[0].x, kv[0].y, kv[0].z, kv[0].w},
-                            {kv[1].x, kv[1].y, kv[1].z, kv[1].w},
-                            {kv[2].x, kv[2].y, kv[2].z, kv[2].w},
-                            {kv[3].x, kv[3].y, kv[3].z, kv[3].w}};
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    out[2 * j] = make_uint2(lo_pair(w[0][j], w[1][j]), lo_pair(w[2][j], w[3][j]));
-    out[2 * j + 1] = make_uint2(hi_pair(w[0][j], w[1][j]), hi_pair(w[2][j], w[3][j]));
-  }
-}
-
-__device__ __forceinline__ bf16x8 as_bf16x8(uint2 a, uint2 b) {
-  uint4 u = make_uint4(a.x, a.y, b.x, b.y);
-  return __builtin_bit_cast(bf16x8, u);
 }
 
 __device__ __forceinline__ bf16x8 pack_p(const f32x16 &s, int base) {
@@ -685,28 +665,24 @@ __global__ void __launch_bounds__(64 * kLongWaves, 8 / kLongWaves) attn_long_ker
 template <int D, int NT>
 struct ShortCfg {
   typedef Dims<D> DM;
-  static constexpr int KL = 32 * NT;             // padded keys = queries
-  static constexpr int V_LD = KL + 4;
-  static constexpr int V_WAVE = DM::DV * V_LD;   // u16 per wave
-  static constexpr int V_TASKS = (KL / 4) * DM::CH;
-  static constexpr int V_PER_L = (V_TASKS + 63) / 64;
-  // Issue all of a head's loads before using any.  Timed at d = 72 with two
-  // query tiles, that needs ~210 registers and runs 1-3% slower than loading
-  // per batch at the same occupancy; with one query tile (L <= 32) or d = 64
-  // it is 10-17% faster.
-  static constexpr bool kHoist = NT == 1 || D % 32 == 0;
+  static constexpr int KL = 32 * NT;                        // padded keys = queries
+  static constexpr int V_BLOCKS = (KL * DM::CH + 63) / 64;  // 1 KB direct-to-LDS loads of V
+  static constexpr int V_WAVE = V_BLOCKS * 512 + 64;        // u16 per wave: V rows, then transpose-read slack
+  // u16 of LDS per workgroup.  With two query tiles it is padded to 54 KB so
+  // that at most two workgroups (two waves per SIMD) share a CU: timed at
+  // 1080p, three waves per SIMD ran 4-13% slower and one wave 10% slower (more
+  // scattered Q/K row loads in flight than the memory system serves well).
+  static constexpr int LDS = NT == 2 && 4 * V_WAVE < 27648 ? 27648 : 4 * V_WAVE;
 };
 
+// At least two waves per SIMD: keeps the compiler from splitting the registers
+// into AGPR accumulators plus VGPRs, which would cost occupancy.
 template <int D, int NT>
-// With hoisted loads, at least two waves per SIMD keeps the compiler from
-// splitting the registers into AGPR accumulators plus VGPRs (which would cost
-// occupancy); the other instantiations keep the default allocation.
-__global__ void __attribute__((amdgpu_flat_work_group_size(1, 256),
-                               amdgpu_waves_per_eu(ShortCfg<D, NT>::kHoist ? 2 : 1)))
+__global__ void __attribute__((amdgpu_flat_work_group_size(1, 256), amdgpu_waves_per_eu(2)))
 attn_short_kernel(AttnArgs a, uint32_t nblocks) {
   typedef ShortCfg<D, NT> C;
   typedef Dims<D> DM;
-  __shared__ __attribute__((aligned(16))) u16 lds[4 * C::V_WAVE];
+  __shared__ __attribute__((aligned(16))) u16 lds[C::LDS];
 
   const uint32_t hg_n = (uint32_t)(a.H + 3) / 4;
   const uint32_t blk = xcd_remap(blockIdx.x, nblocks);
@@ -719,110 +695,81 @@ attn_short_kernel(AttnArgs a, uint32_t nblocks) {
   const int64_t rs = (int64_t)a.H * D;
   u16 *Vs = lds + wave * C::V_WAVE;
 
-  // constant V^T rows [D, DV)
-  for (int i = lane; i < (DM::DV - D) * C::V_LD; i += 64) {
-    const int dd = D + i / C::V_LD;
-    Vs[dd * C::V_LD + i % C::V_LD] = (DM::ONES && dd == D) ? (u16)0x3F80 : (u16)0;
-  }
+  // V^T operand by transpose reads of V stored [key][d] (the layout of the
+  // long kernel): lane 4j + q of 16-lane group G addresses V[key0 + j][dg + 4q].
+  const int grp = lane >> 4, gi = lane & 15;
+  const int v_off = (gi >> 2) * D + 16 * (grp & 1) + 4 * (gi & 3) + 4 * (grp >> 1) * D;
+  const int dlast = 32 * (DM::DT - 1) + l32;   // O^T row of this lane in the last tile
+  const bool vkeep = dlast < D;
+  const uint32_t vconst = (DM::ONES && dlast == D) ? 0x3F803F80u : 0u;
+
+  // Blocks of V rows wholly past L are never loaded: they are zeroed once, so
+  // the P.V products of those (masked) keys are 0 * 0.
+  const int vblk = min(C::V_BLOCKS, (L * DM::CH + 63) / 64);   // blocks loaded per head
+  for (int i = vblk * 64 + lane; i < C::V_BLOCKS * 64; i += 64) reinterpret_cast<uint4 *>(Vs)[i] = make_uint4(0, 0, 0, 0);
 
   for (int h = h0 + wave; h < h1; h += 4) {
     const int64_t base = outer * L * rs + (int64_t)h * D;
     const u16 *qp = a.q + base, *kp = a.k + base, *vp = a.v + base;
     u16 *op = a.o + base;
 
-    // With kHoist every global load of the head is issued before any of them
-    // is used, so the wave waits for memory once per head.  Addresses are then
-    // clamped instead of branched on: rows past L re-read row L-1 (V^T zeroes
-    // them below; Q and K rows past L only feed queries that are not stored and
-    // keys that are masked) and Q/K chunks past d re-read the last chunk
-    // (zeroed below).  Without it, loads sit under their bounds checks.
-    uint4 vraw[C::V_PER_L][4], qraw[NT][DM::KS], kraw[NT][DM::KS];
-    if constexpr (C::kHoist) {
+    // Q and K go straight into operand registers; all loads are issued before
+    // any is used.  Rows past L re-read row L-1 (those queries are not stored,
+    // those keys are masked); chunks past d re-read the last chunk and are
+    // zeroed below.
+    uint4 qraw[NT][DM::KS], kraw[NT][DM::KS];
 #pragma unroll
-      for (int i = 0; i < C::V_PER_L; ++i) {
-        const int task = min(lane + 64 * i, C::V_TASKS - 1);
-        const int key4 = task % (C::KL / 4), ch = task / (C::KL / 4);
+    for (int nt = 0; nt < NT; ++nt) {
+      const int64_t row = min(nt * 32 + l32, L - 1);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int key = min(key4 * 4 + j, L - 1);
-          vraw[i][j] = *reinterpret_cast<const uint4 *>(vp + (int64_t)key * rs + ch * 8);
-        }
-      }
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const int64_t row = min(nt * 32 + l32, L - 1);
-#pragma unroll
-        for (int ks = 0; ks < DM::KS; ++ks) {
-          const int dd = min(ks * 16 + g * 8, D - 8);
-          qraw[nt][ks] = *reinterpret_cast<const uint4 *>(qp + row * rs + dd);
-          kraw[nt][ks] = *reinterpret_cast<const uint4 *>(kp + row * rs + dd);
-        }
+      for (int ks = 0; ks < DM::KS; ++ks) {
+        const int dd = min(ks * 16 + g * 8, D - 8);
+        qraw[nt][ks] = *reinterpret_cast<const uint4 *>(qp + row * rs + dd);
+        kraw[nt][ks] = *reinterpret_cast<const uint4 *>(kp + row * rs + dd);
       }
     }
-
-    // V^T of this head into the wave's LDS slice
+    // V rows go global -> LDS directly: 16-byte chunk n of the packed
+    // [key][d] tile is chunk n % (d/8) of key n / (d/8); keys past L re-read
+    // row L-1 (their probabilities are 0) and chunks past the tile land in
+    // the slack.
 #pragma unroll
-    for (int i = 0; i < C::V_PER_L; ++i) {
-      const int task = lane + 64 * i;
-      if (task < C::V_TASKS) {
-        const int key4 = task % (C::KL / 4), ch = task / (C::KL / 4);
-        uint4 kv[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int key = key4 * 4 + j;
-          if constexpr (C::kHoist)
-            kv[j] = key < L ? vraw[i][j] : make_uint4(0, 0, 0, 0);
-          else
-            kv[j] = key < L ? *reinterpret_cast<const uint4 *>(vp + (int64_t)key * rs + ch * 8) : make_uint4(0, 0, 0, 0);
-        }
-        uint2 tr[8];
-        transpose4x8(kv, tr);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) *reinterpret_cast<uint2 *>(Vs + (ch * 8 + j) * C::V_LD + key4 * 4) = tr[j];
-      }
+    for (int b = 0; b < C::V_BLOCKS; ++b) {
+      if (b >= vblk) break;
+      const int n = 64 * b + lane;
+      const int key = min(n / DM::CH, L - 1), ch = n % DM::CH;
+      __builtin_amdgcn_global_load_lds(vp + (int64_t)key * rs + ch * 8,
+                                       (__attribute__((address_space(3))) void *)(Vs + b * 512), 16, 0, 0);
     }
     bf16x8 qf[NT][DM::KS], kf[NT][DM::KS];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int row = nt * 32 + l32;
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int ks = 0; ks < DM::KS; ++ks) {
-        const int dd = ks * 16 + g * 8;
-        uint4 uq = make_uint4(0, 0, 0, 0), uk = make_uint4(0, 0, 0, 0);
-        if constexpr (C::kHoist) {
-          if (dd < D) {
-            uq = qraw[nt][ks];
-            uk = kraw[nt][ks];
-          }
-        } else if (row < L && dd < D) {
-          uq = *reinterpret_cast<const uint4 *>(qp + (int64_t)row * rs + dd);
-          uk = *reinterpret_cast<const uint4 *>(kp + (int64_t)row * rs + dd);
-        }
-        qf[nt][ks] = __builtin_bit_cast(bf16x8, uq);
-        kf[nt][ks] = __builtin_bit_cast(bf16x8, uk);
+        const bool pad = ks * 16 + g * 8 >= D;
+        qf[nt][ks] = __builtin_bit_cast(bf16x8, pad ? make_uint4(0, 0, 0, 0) : qraw[nt][ks]);
+        kf[nt][ks] = __builtin_bit_cast(bf16x8, pad ? make_uint4(0, 0, 0, 0) : kraw[nt][ks]);
       }
-    }
-    // S^T[mt][nt]: keys of tile mt x queries of tile nt
-    f32x16 s[NT][NT];
-#pragma unroll
-    for (int mt = 0; mt < NT; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[mt][nt][r] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < DM::KS; ++ks)
-          s[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[mt][ks], qf[nt][ks], s[mt][nt], 0, 0, 0);
-      }
+
+    // One query tile at a time: S^T of its key tiles, softmax, bf16 P^T.
+    bf16x8 pf[NT][NT][2];   // [query tile][key tile][16-key half]
+    float lsum[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
+      f32x16 s[NT];   // keys of tile mt x the queries of tile nt
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[mt][r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < DM::KS; ++ks) s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[mt][ks], qf[nt][ks], s[mt], 0, 0, 0);
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float x = (mt * 32 + acc_row(r, g) < nv) ? s[mt][nt][r] : -INFINITY;
-          s[mt][nt][r] = x;
+          const float x = (mt * 32 + acc_row(r, g) < nv) ? s[mt][r] : -INFINITY;
+          s[mt][r] = x;
           mx = fmaxf(mx, x);
         }
       mx = max_across_halves(mx);
@@ -830,75 +777,71 @@ attn_short_kernel(AttnArgs a, uint32_t nblocks) {
 #pragma unroll
       for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[mt][nt][r] = __builtin_amdgcn_exp2f(fmaf(s[mt][nt][r], a.c, -mc));
-    }
-    // V^T is complete in LDS once every lane's stores have issued (one wave)
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    f32x16 oacc[DM::DT][NT];
-#pragma unroll
-    for (int dt = 0; dt < DM::DT; ++dt)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[dt][nt][r] = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < NT; ++mt)
-#pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2) {
-        bf16x8 pf[NT];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) pf[nt] = pack_p(s[mt][nt], ks2 * 8);
-        const int kk = mt * 32 + ks2 * 16 + g * 4;
-#pragma unroll
-        for (int dt = 0; dt < DM::DT; ++dt) {
-          const u16 *vrow = Vs + (dt * 32 + l32) * C::V_LD + kk;
-          const bf16x8 vf = as_bf16x8(*reinterpret_cast<const uint2 *>(vrow), *reinterpret_cast<const uint2 *>(vrow + 8));
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
-            oacc[dt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[nt], oacc[dt][nt], 0, 0, 0);
-        }
-      }
-    float lsum[NT];
-    if constexpr (!DM::ONES) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
+        for (int r = 0; r < 16; ++r) s[mt][r] = __builtin_amdgcn_exp2f(fmaf(s[mt][r], a.c, -mc));
+      if constexpr (!DM::ONES) {
         float acc = 0.f;
 #pragma unroll
         for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc += s[mt][nt][r];
+          for (int r = 0; r < 16; ++r) acc += s[mt][r];
         lsum[nt] = acc + __shfl_xor(acc, 32);
       }
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt) {
+        pf[nt][mt][0] = pack_p(s[mt], 0);
+        pf[nt][mt][1] = pack_p(s[mt], 8);
+      }
     }
+    // V has landed in this wave's slice
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
+      f32x16 oacc[DM::DT];
+#pragma unroll
+      for (int dt = 0; dt < DM::DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt)
+#pragma unroll
+        for (int ks2 = 0; ks2 < 2; ++ks2) {
+          const u16 *vb = Vs + (mt * 32 + ks2 * 16) * D + v_off;
+#pragma unroll
+          for (int dt = 0; dt < DM::DT; ++dt) {
+            uint4 u = tr_read_pair<D>(vb + dt * 32);
+            if (DM::DV != D && dt == DM::DT - 1 && !vkeep) u = make_uint4(vconst, vconst, vconst, vconst);
+            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u), pf[nt][mt][ks2], oacc[dt],
+                                                               0, 0, 0);
+          }
+        }
       float l;
       if constexpr (DM::ONES) {
-        l = __shfl(oacc[DM::ONES_DT][nt][DM::ONES_R], l32);
+        l = __shfl(oacc[DM::ONES_DT][DM::ONES_R], l32);
       } else {
         l = lsum[nt];
       }
       const float inv = 1.0f / l;
       const int qi = nt * 32 + l32;
-      if (qi >= L) continue;
-      u16 *orow = op + (int64_t)qi * rs;
+      if (qi < L) {
+        u16 *orow = op + (int64_t)qi * rs;
 #pragma unroll
-      for (int dt = 0; dt < DM::DT; ++dt)
+        for (int dt = 0; dt < DM::DT; ++dt)
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-          const int dd = dt * 32 + rb * 8 + g * 4;
-          if (dd + 4 <= D) {
-            uint2 w;
-            w.x = pack_bf16x2(oacc[dt][nt][rb * 4 + 0] * inv, oacc[dt][nt][rb * 4 + 1] * inv);
-            w.y = pack_bf16x2(oacc[dt][nt][rb * 4 + 2] * inv, oacc[dt][nt][rb * 4 + 3] * inv);
-            *reinterpret_cast<uint2 *>(orow + dd) = w;
+          for (int rb = 0; rb < 4; ++rb) {
+            const int dd = dt * 32 + rb * 8 + g * 4;
+            if (dd + 4 <= D) {
+              uint2 w;
+              w.x = pack_bf16x2(oacc[dt][rb * 4 + 0] * inv, oacc[dt][rb * 4 + 1] * inv);
+              w.y = pack_bf16x2(oacc[dt][rb * 4 + 2] * inv, oacc[dt][rb * 4 + 3] * inv);
+              *reinterpret_cast<uint2 *>(orow + dd) = w;
+            }
           }
-        }
+      }
     }
-    // the next head overwrites V^T: all lanes' reads of this head are done
+    // the next head overwrites V: all lanes' reads of this head are done
+    __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
