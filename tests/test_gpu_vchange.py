@@ -55,6 +55,9 @@ def run(vn, vc, rows, H, d, thr, dt, update, with_idx=True):
     (257, 3, 64, 4.0, BF, 0),
     (100, 2, 128, 10.0, BF, 1),
     (90, 5, 72, 6.0, F32, 1),
+    (77, 3, 40, 3.0, BF, 1),          # 5 pieces a row: 12 rows per wavefront pass, 4 idle lanes
+    (41, 2, 128, 10.0, F32, 1),       # 32 pieces a row: 2 rows per pass
+    (500, 1, 24, 2.0, BF, 0),         # 3 pieces a row
     (33, 7, 8, 0.0, BF, 1),           # threshold 0: every vector that changed at all
     (50, 2, 16, float("inf"), F32, 1),  # nothing is active
     (0, 4, 72, 1.0, BF, 1),           # no rows
