@@ -6,10 +6,12 @@
 // scaled scores; the union's output weights each part by exp(lse_part -
 // lse_union).
 //
-// A group of LPR lanes of one wavefront handles a (sequence, query, head) row:
-// the lanes cover its 16-byte vectors, so a group reads one contiguous row.
-// A row never straddles wavefronts and every lane issues its reads of both
-// parts before any write, so the merge may run in place on either input.
+// Rows (one per (sequence, query, head)) that start 16-byte aligned and have
+// at most 64 16-byte pieces take the contiguous-pass kernel: a wavefront pass
+// covers floor(64 / pieces) consecutive rows as one contiguous run.  Other
+// rows take a group of LPR lanes per row.  In both, a row never straddles
+// wavefronts and every lane issues its reads of both parts before any write,
+// so the merge may run in place on either input.
 // HBM-bound: per row, two rows and two log-sum-exps in, one of each out.
 #include <math.h>
 
@@ -72,6 +74,62 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(const T *oa, const floa
   }
 }
 
+// Rows of 16-byte-aligned rows with P <= 64 pieces: a wavefront pass takes
+// floor(64 / P) consecutive rows as one contiguous run (lane l holds piece l),
+// U passes of loads in flight; every lane of a row reads the same two
+// log-sum-exps.  I is the index type (32-bit when every row index fits).
+template <typename T, typename I, int U>
+__global__ void __launch_bounds__(256) attn_merge_flat_kernel(const T *oa, const float *la, const T *ob,
+                                                              const float *lb, I rows, I L, I H, int P, T *o,
+                                                              float *lse) {
+  constexpr int VW = 16 / sizeof(T);            // elements per 16-byte vector
+  const int lane = threadIdx.x & 63;
+  const int rpw = 64 / P;                       // rows per wavefront pass
+  const int rl = lane / P, j = lane - rl * P;   // row within the pass, piece within the row
+  const bool used = rl < rpw;
+  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
+  const int64_t step = (int64_t)rpw * U;
+  for (int64_t r00 = wave * step; r00 < (int64_t)rows; r00 += nwaves * step) {   // uniform per wavefront
+    uint4 x[U], y[U];
+    float fa[U], fb[U], ln[U];
+    I li[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t r = r00 + u * rpw + rl;     // row in [outer, L, H] order
+      x[u] = y[u] = make_uint4(0, 0, 0, 0);
+      fa[u] = fb[u] = ln[u] = 0.f;
+      li[u] = 0;
+      if (used && r < (int64_t)rows) {
+        const int64_t off = ((r00 + u * rpw) * P + lane) * VW;
+        x[u] = *reinterpret_cast<const uint4 *>(oa + off);
+        y[u] = *reinterpret_cast<const uint4 *>(ob + off);
+        const I ri = (I)r, h = ri % H, ql = ri / H;   // ql = outer * L + query
+        li[u] = (ql / L * H + h) * L + ql % L;
+        const float a = la[li[u]], b = lb[li[u]];
+        const float m = fmaxf(a, b);
+        const bool empty = m == -INFINITY;      // neither part has a valid key
+        const float wa = empty ? 0.f : expf(a - m), wb = empty ? 0.f : expf(b - m);
+        const float tot = wa + wb;
+        fa[u] = empty ? 0.f : wa / tot;
+        fb[u] = empty ? 0.f : wb / tot;
+        ln[u] = empty ? -INFINITY : m + logf(tot);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t r = r00 + u * rpw + rl;
+      if (!used || r >= (int64_t)rows) continue;
+      const T *xe = reinterpret_cast<const T *>(&x[u]), *ye = reinterpret_cast<const T *>(&y[u]);
+      T z[VW];
+#pragma unroll
+      for (int e = 0; e < VW; ++e) z[e] = Elem<T>::store(fmaf(fa[u], Elem<T>::load(xe[e]), fb[u] * Elem<T>::load(ye[e])));
+      *reinterpret_cast<uint4 *>(o + ((r00 + u * rpw) * P + lane) * VW) = *reinterpret_cast<const uint4 *>(z);
+      if (j == 0) lse[li[u]] = ln[u];
+    }
+  }
+}
+
 template <typename T>
 __global__ void __launch_bounds__(256) attn_empty_kernel(T *o, float *lse, int64_t n_o, int64_t n_lse) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -90,10 +148,32 @@ void merge_launch(const void *o_a, const float *lse_a, const void *o_b, const fl
                      static_cast<const T *>(o_b), lse_b, rows, L, H, d, static_cast<T *>(o), lse);
 }
 
+template <typename T>
+void merge_flat_launch(const void *o_a, const float *lse_a, const void *o_b, const float *lse_b, int64_t rows, int L,
+                       int H, int P, void *o, float *lse, hipStream_t s) {
+  constexpr int U = 4;                                  // passes whose loads are issued together
+  const int64_t step = (int64_t)(64 / P) * U;           // rows per wavefront iteration
+  const int64_t waves = (rows + step - 1) / step;
+  const uint32_t blocks = (uint32_t)std::min<int64_t>((waves + 3) / 4, 256 * 64);
+  const T *a = static_cast<const T *>(o_a), *b = static_cast<const T *>(o_b);
+  if (rows < (1ll << 31))
+    hipLaunchKernelGGL((attn_merge_flat_kernel<T, int32_t, U>), dim3(blocks), dim3(256), 0, s, a, lse_a, b, lse_b,
+                       (int32_t)rows, (int32_t)L, (int32_t)H, P, static_cast<T *>(o), lse);
+  else
+    hipLaunchKernelGGL((attn_merge_flat_kernel<T, int64_t, U>), dim3(blocks), dim3(256), 0, s, a, lse_a, b, lse_b,
+                       rows, (int64_t)L, (int64_t)H, P, static_cast<T *>(o), lse);
+}
+
 st_status launch_attn_merge(const void *o_a, const float *lse_a, const void *o_b, const float *lse_b, int64_t outer,
                             int L, int H, int d, int elem_bytes, void *o, float *lse, hipStream_t s) {
   const int64_t rows = outer * L * H;
   if (rows == 0) return ST_OK;
+  const int pieces = d * elem_bytes / 16;
+  if ((d * elem_bytes) % 16 == 0 && pieces <= 64) {
+    if (elem_bytes == 2) merge_flat_launch<u16>(o_a, lse_a, o_b, lse_b, rows, L, H, pieces, o, lse, s);
+    else merge_flat_launch<float>(o_a, lse_a, o_b, lse_b, rows, L, H, pieces, o, lse, s);
+    return launch_status();
+  }
   // lanes per row: enough for the row's 16-byte vectors (or elements), a power of two
   const int units = (d * elem_bytes) % 16 == 0 ? d * elem_bytes / 16 : d;
   const int lpr = units <= 8 ? 8 : units <= 16 ? 16 : units <= 32 ? 32 : 64;

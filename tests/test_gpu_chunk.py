@@ -129,7 +129,9 @@ def test_chunked_then_merged_equals_unchunked(dt, d, cuts, valid):
     check_lse(acc_l, rl, dt, "merged lse")
 
 
-@pytest.mark.parametrize("dt,d", [(BF, 72), (F32, 64), (BF, 5)])
+# d = 40 (5 pieces a row, idle lanes in a pass), fp32 d = 72 (18 pieces), d = 520 (65 pieces: per-row lane
+# groups), d = 5 (rows not 16-byte aligned: per-row lane groups, element by element)
+@pytest.mark.parametrize("dt,d", [(BF, 72), (F32, 64), (BF, 40), (F32, 72), (BF, 520), (BF, 5)])
 def test_merge_matches_oracle_including_empty_parts(dt, d):
     outer, L, H = 3, 77, 4
     sd = "bf16" if dt == BF else "f32"
