@@ -290,7 +290,11 @@ typedef struct {
  * 2D RoPE with global (h, w)), the temporal layer once per space slice
  * (S/N_S patches, all T frames, 1D RoPE with global t, keys t >= t_valid
  * masked); the result is rearranged back to y [B, T, S, C].
- * n_t = n_s = 1 is the unsliced layer pair.
+ * n_t = n_s = 1 is the unsliced layer pair.  In bf16 the rearranges and the
+ * per-slice gathers and scatters move no data of their own: each slice's QKV
+ * projection reads its rows from where they lie and its output projection
+ * stores them where the next phase (or y) expects them.  fp32 runs them as
+ * explicit copies.
  *
  *   x         in   [B, T, S, C]   bf16: C and H*d multiples of 64.
  *                                 T % n_t == 0, S % n_s == 0 (the caller pads T

@@ -13,7 +13,7 @@ namespace {
 
 // y[r, n] = sum_k a[r, k] * w[n, k]; output row r of column n goes to
 // dst_for(n) with its own row stride (q/k/v split) or to y.
-__global__ void linear_f32_kernel(const float *a, int64_t rows, int K, const float *w, int N, float *y, RowSwap sw) {
+__global__ void linear_f32_kernel(const float *a, int64_t rows, int K, const float *w, int N, float *y, RowMap ym) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= rows * N) return;
   const int64_t r = i / N;
@@ -21,7 +21,7 @@ __global__ void linear_f32_kernel(const float *a, int64_t rows, int K, const flo
   const float *ar = a + r * K, *wr = w + (int64_t)n * K;
   float acc = 0.f;
   for (int k = 0; k < K; ++k) acc = fmaf(ar[k], wr[k], acc);
-  y[swap_row(r, sw) * N + n] = acc;
+  y[map_row(r, ym) * N + n] = acc;
 }
 
 __global__ void qkv_f32_kernel(const float *x, int64_t rows, int K, const float *w, int H, int d, float *q,
@@ -145,11 +145,11 @@ st_status launch_qkv_f32(const float *x, int64_t rows, int c_in, const float *w,
 }
 
 st_status launch_linear_f32(const float *a, int64_t rows, int k_in, const float *w, int n_out, float *y,
-                            hipStream_t s, RowSwap sw) {
+                            hipStream_t s, RowMap ym) {
   if (rows == 0) return ST_OK;
   const int64_t n = rows * n_out;
   if (blocks_for(n) >= (1u << 31)) return ST_EUNSUPPORTED;
-  hipLaunchKernelGGL(linear_f32_kernel, dim3(blocks_for(n)), dim3(256), 0, s, a, rows, k_in, w, n_out, y, sw);
+  hipLaunchKernelGGL(linear_f32_kernel, dim3(blocks_for(n)), dim3(256), 0, s, a, rows, k_in, w, n_out, y, ym);
   return launch_status();
 }
 

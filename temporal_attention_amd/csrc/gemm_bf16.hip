@@ -53,7 +53,8 @@ struct GemmArgs {
   int K, N;
   // plain output
   u16 *y;            // [M, N], rows permuted by sw
-  RowSwap sw;
+  RowMap ymap;       // MODE 0: row r of the product is stored at row map_row(r, ymap) of y
+  RowMap xmap;       // with XMAP: row r of the product reads row map_row(r, xmap) of x
   // qkv output
   u16 *q, *k, *v;    // [M, H, D]
   int H;
@@ -85,11 +86,14 @@ __device__ __forceinline__ int slot_of(int row, int kc) { return row * 8 + (kc ^
 // Global -> LDS loads of one stage: 1 KB (8 whole rows) per wavefront
 // instruction, lane l of block b filling slot 64 b + l.  Each lane's element offset inside the K
 // window is fixed for the whole K loop and computed once; rows past M or N
-// repeat the last row (their results are never stored).
-template <int CT>
+// repeat the last row (their results are never stored).  With XMAP the x rows
+// go through a.xmap and their offsets are from a.x (64-bit), else from the
+// tile's first row.
+template <int CT, bool XMAP>
 struct GemmDma {
   typedef Tile<CT> TL;
-  int off[TL::PER_WAVE];
+  typedef typename std::conditional<XMAP, int64_t, int>::type Off;
+  Off off[TL::PER_WAVE];
 
   __device__ __forceinline__ void init(const GemmArgs &a, int64_t m0, int n0, int lane, int wave) {
 #pragma unroll
@@ -99,8 +103,12 @@ struct GemmDma {
       const int sl = (isb ? n - TL::A_BLOCKS : n) * 64 + lane;
       const int row = sl >> 3;
       const int kc = (sl & 7) ^ (row & 7);
-      const int r = isb ? (int)(min<int64_t>(m0 + row, a.M - 1) - m0) : min(n0 + row, a.N - 1);
-      off[i] = r * a.K + 8 * kc;
+      if (XMAP && isb) {
+        off[i] = map_row(min<int64_t>(m0 + row, a.M - 1), a.xmap) * a.K + 8 * kc;
+      } else {
+        const int r = isb ? (int)(min<int64_t>(m0 + row, a.M - 1) - m0) : min(n0 + row, a.N - 1);
+        off[i] = r * a.K + 8 * kc;
+      }
     }
   }
 
@@ -122,9 +130,9 @@ struct GemmDma {
 // One K step for one wave: issue the next step's loads into `nxt`, then
 // 2 x CT x 4 MFMAs on the stage in As / Bs.  Stage pointers are restrict-qualified:
 // the loads in flight never alias the stage being read.
-template <int CT>
+template <int CT, bool XMAP>
 __device__ __forceinline__ void gemm_step(const u16 *__restrict__ As, const u16 *__restrict__ Bs,
-                                          u16 *__restrict__ nxt, bool prefetch, int k_next, const GemmDma<CT> &dma,
+                                          u16 *__restrict__ nxt, bool prefetch, int k_next, const GemmDma<CT, XMAP> &dma,
                                           const u16 *xb, const u16 *w, int wave, int wn, int wm, int l16, int g4,
                                           f32x4 (&acc)[CT][kTT]) {
   typedef Tile<CT> TL;
@@ -157,7 +165,7 @@ __device__ __forceinline__ int64_t rope_table_floats(const RopeArgs &r) {
 }
 
 // MODE 0: plain output y.  MODE 1: q/k/v with RMSNorm + RoPE on q, k (head dim D).
-template <int CT, int MODE, int D>
+template <int CT, int MODE, int D, bool XMAP>
 __global__ void __launch_bounds__(kThreads, 1) gemm_bf16_kernel(GemmArgs a, uint32_t n_tiles_n, uint32_t nblocks) {
   typedef Tile<CT> TL;
   __shared__ __attribute__((aligned(16))) u16 lds[kStages * TL::STAGE];
@@ -185,9 +193,9 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_bf16_kernel(GemmArgs a, uint
 #pragma unroll
     for (int j = 0; j < kTT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  GemmDma<CT> dma;
+  GemmDma<CT, XMAP> dma;
   dma.init(a, m0, n0, lane, wave);
-  const u16 *xb = a.x + m0 * a.K;
+  const u16 *xb = XMAP ? a.x : a.x + m0 * a.K;
   const int nk = a.K / kBK;
   // MODE 1: the RoPE table moves into the stage the last K step leaves free
   // (its loads overlap that step's MFMAs), so the epilogue's cos/sin reads are
@@ -211,7 +219,8 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_bf16_kernel(GemmArgs a, uint
                                          16, 0, 0);
       }
     }
-    gemm_step<CT>(cur, cur + TL::LDS_A, nxt, kt + 1 < nk, (kt + 1) * kBK, dma, xb, a.w, wave, wn, wm, l16, g4, acc);
+    gemm_step<CT, XMAP>(cur, cur + TL::LDS_A, nxt, kt + 1 < nk, (kt + 1) * kBK, dma, xb, a.w, wave, wn, wm, l16, g4,
+                        acc);
     wait_vmem_upto<0>();
     __syncthreads();
   }
@@ -223,7 +232,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_bf16_kernel(GemmArgs a, uint
     for (int tt = 0; tt < kTT; ++tt) {
       const int64_t r = m0 + wm * kWM + tt * 16 + l16;
       if (r >= a.M) continue;
-      u16 *yr = a.y + swap_row(r, a.sw) * a.N;
+      u16 *yr = a.y + map_row(r, a.ymap) * a.N;
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
         const int n = nw0 + ct * 16 + g4 * 4;
@@ -371,7 +380,7 @@ __device__ __forceinline__ void epilogue_qkv(const GemmArgs &a, f32x4 (&acc)[CT]
   else pass2(std::true_type{});
 }
 
-template <int CT, int MODE, int D>
+template <int CT, int MODE, int D, bool XMAP = false>
 st_status launch_gemm(const GemmArgs &a, hipStream_t s) {
   typedef Tile<CT> TL;
   if (a.M == 0) return ST_OK;
@@ -379,14 +388,16 @@ st_status launch_gemm(const GemmArgs &a, hipStream_t s) {
   const uint32_t nt = (a.N + TL::BN - 1) / TL::BN;
   const int64_t nb = mt * nt;
   if (nb >= (1ll << 31)) return ST_EUNSUPPORTED;
-  hipLaunchKernelGGL((gemm_bf16_kernel<CT, MODE, D>), dim3((uint32_t)nb), dim3(kThreads), 0, s, a, nt, (uint32_t)nb);
+  hipLaunchKernelGGL((gemm_bf16_kernel<CT, MODE, D, XMAP>), dim3((uint32_t)nb), dim3(kThreads), 0, s, a, nt,
+                     (uint32_t)nb);
   return launch_status();
 }
 
 }  // namespace
 
 st_status launch_qkv_bf16(const void *x, int64_t rows, int c_in, const void *w, const float *g_q, const float *g_k,
-                          float eps, const RopeArgs &rope, int H, int d, void *q, void *k, void *v, hipStream_t s) {
+                          float eps, const RopeArgs &rope, int H, int d, void *q, void *k, void *v, hipStream_t s,
+                          RowMap xmap) {
   GemmArgs a{};
   a.x = static_cast<const u16 *>(x);
   a.w = static_cast<const u16 *>(w);
@@ -401,16 +412,18 @@ st_status launch_qkv_bf16(const void *x, int64_t rows, int c_in, const void *w, 
   a.g_k = g_k;
   a.eps = eps;
   a.rope = rope;
+  a.xmap = xmap;
+  const bool mapped = xmap.n1 != 0;
   switch (d) {
-    case 72: return launch_gemm<9, 1, 72>(a, s);    // wave = 2 heads x 72
-    case 64: return launch_gemm<8, 1, 64>(a, s);    // wave = 2 heads x 64
-    case 128: return launch_gemm<8, 1, 128>(a, s);  // wave = 1 head x 128
+    case 72: return mapped ? launch_gemm<9, 1, 72, true>(a, s) : launch_gemm<9, 1, 72>(a, s);   // 2 heads x 72
+    case 64: return mapped ? launch_gemm<8, 1, 64, true>(a, s) : launch_gemm<8, 1, 64>(a, s);   // 2 heads x 64
+    case 128: return mapped ? launch_gemm<8, 1, 128, true>(a, s) : launch_gemm<8, 1, 128>(a, s);   // 1 head x 128
     default: return ST_EUNSUPPORTED;
   }
 }
 
 st_status launch_linear_bf16(const void *a_, int64_t rows, int k_in, const void *w, int n_out, void *y,
-                             hipStream_t s, RowSwap sw) {
+                             hipStream_t s, RowMap ymap) {
   GemmArgs a{};
   a.x = static_cast<const u16 *>(a_);
   a.w = static_cast<const u16 *>(w);
@@ -418,7 +431,7 @@ st_status launch_linear_bf16(const void *a_, int64_t rows, int k_in, const void 
   a.K = k_in;
   a.N = n_out;
   a.y = static_cast<u16 *>(y);
-  a.sw = sw;
+  a.ymap = ymap;
   if (n_out % 288 == 0) return launch_gemm<9, 0, 0>(a, s);
   return launch_gemm<8, 0, 0>(a, s);
 }

@@ -42,17 +42,20 @@ st_status check_rope(int kind, const float *table, int npos, int64_t period, int
 }
 
 // ---------------------------------------------------------------- dispatch
+// xmap (bf16 only): row r of the projection reads row map_row(r, xmap) of x.
 st_status do_qkv(const void *x, int64_t rows, int c_in, const void *w, const float *gq, const float *gk, float eps,
-                 const RopeArgs &rope, int H, int d, int dt, void *q, void *k, void *v, hipStream_t s) {
-  if (dt == ST_BF16) return launch_qkv_bf16(x, rows, c_in, w, gq, gk, eps, rope, H, d, q, k, v, s);
+                 const RopeArgs &rope, int H, int d, int dt, void *q, void *k, void *v, hipStream_t s,
+                 RowMap xmap = {}) {
+  if (dt == ST_BF16) return launch_qkv_bf16(x, rows, c_in, w, gq, gk, eps, rope, H, d, q, k, v, s, xmap);
+  if (xmap.n1 != 0) return ST_EUNSUPPORTED;
   return launch_qkv_f32((const float *)x, rows, c_in, (const float *)w, gq, gk, eps, rope, H, d, (float *)q,
                         (float *)k, (float *)v, s);
 }
 
 st_status do_linear(const void *a, int64_t rows, int k_in, const void *w, int n_out, int dt, void *y, hipStream_t s,
-                    RowSwap sw = {}) {
-  if (dt == ST_BF16) return launch_linear_bf16(a, rows, k_in, w, n_out, y, s, sw);
-  return launch_linear_f32((const float *)a, rows, k_in, (const float *)w, n_out, (float *)y, s, sw);
+                    RowMap ymap = {}) {
+  if (dt == ST_BF16) return launch_linear_bf16(a, rows, k_in, w, n_out, y, s, ymap);
+  return launch_linear_f32((const float *)a, rows, k_in, (const float *)w, n_out, (float *)y, s, ymap);
 }
 
 st_status do_attn(const void *q, const void *k, const void *v, int64_t outer, int L, int nv, int H, int d, float scale,
@@ -108,17 +111,18 @@ BlockPlan plan_block(int B, int T, int S, int grid_w, int C, int H, int d, int n
   return p;
 }
 
-// One layer: projection + norm/RoPE, attention, output projection (its rows
-// optionally stored in swapped order, which fuses the following relayout).
+// One layer: projection + norm/RoPE, attention, output projection.  The
+// projection may read its rows through xmap and the output projection store
+// them through ymap, which fuses a relayout on either side into the layer.
 st_status run_layer(const void *x, int64_t outer, int L, int nv, int C, int H, int d, const st_layer_weights *w,
                     float eps, const RopeArgs &rope, int dt, void *q, void *k, void *v, void *o, void *y,
-                    bool temporal, hipStream_t s, RowSwap sw = {}) {
+                    bool temporal, hipStream_t s, RowMap ymap = {}, RowMap xmap = {}) {
   const int64_t rows = outer * L;
-  st_status r = do_qkv(x, rows, C, w->w_qkv, w->g_q, w->g_k, eps, rope, H, d, dt, q, k, v, s);
+  st_status r = do_qkv(x, rows, C, w->w_qkv, w->g_q, w->g_k, eps, rope, H, d, dt, q, k, v, s, xmap);
   if (r != ST_OK) return r;
   r = do_attn(q, k, v, outer, L, nv, H, d, (float)(1.0 / sqrt((double)d)), dt, o, temporal, s);
   if (r != ST_OK) return r;
-  return do_linear(o, rows, H * d, w->w_o, C, dt, y, s, sw);
+  return do_linear(o, rows, H * d, w->w_o, C, dt, y, s, ymap);
 }
 
 // Events that order the two streams of the pipelined slicing schedule.  A
@@ -224,15 +228,69 @@ st_status block_sliced(const void *x, int B, int T, int t_valid, int S, int grid
     // rows (b, t, s) are stored as rows (b, s, t) of the temporal input, and
     // the temporal layer's rows (b, s, t) as rows (b, t, s) of y.
     void *hs = W + P.xs;
-    r = run_layer(x, (int64_t)B * T, S, S, C, H, d, spatial, eps, r2, dtype, q, k, v, o, hs, false, s, RowSwap{T, S});
+    r = run_layer(x, (int64_t)B * T, S, S, C, H, d, spatial, eps, r2, dtype, q, k, v, o, hs, false, s, row_swap(T, S));
     if (r != ST_OK) return r;
     return run_layer(hs, (int64_t)B * S, T, t_valid, C, H, d, temporal, eps, r1, dtype, q, k, v, o, y, true, s,
-                     RowSwap{S, T});
+                     row_swap(S, T));
   }
 
-  // Sliced schedule.  Blocked layout xb[b][i][j][a][e][c] with a < T/N_T, e < S/N_S.
-  // Relayouts run on `side`, layers on `s`; with one stream this is the plain
-  // order of the pseudocode.
+  const int tt = T / n_t, ss_ = S / n_s;
+  if (side == s && dtype == ST_BF16) {
+    // Sliced schedule on one stream with every relayout fused into the layers'
+    // row addressing: time slice i's projection reads its rows of x where they
+    // lie and its output projection stores them into the blocked layout
+    // hb[b][i][j][a][e] (a < T/N_T, e < S/N_S); space slice j's projection reads
+    // its rows from hb and its output projection stores them at their place in
+    // y.  Each slice runs the same kernels on the same rows as with explicit
+    // gathers and scatters, so the results are bit-identical to those.
+    const int64_t TS = (int64_t)T * S, blk = (int64_t)tt * ss_;
+    void *hb = W + P.hb;
+    for (int i = 0; i < n_t; ++i) {
+      RowMap xm;   // slice row (b, a*S + s) -> x row b*T*S + i*tt*S + a*S + s
+      xm.n1 = 1;
+      xm.n3 = (int64_t)tt * S;
+      xm.s0 = TS;
+      xm.s3 = 1;
+      xm.base = (int64_t)i * tt * S;
+      RowMap ym;   // slice row (b, a, j, e), s = j*ss + e -> hb row ((b*N_T + i)*N_S + j)*tt*ss + a*ss + e
+      ym.n1 = tt;
+      ym.n2 = n_s;
+      ym.n3 = ss_;
+      ym.s0 = TS;
+      ym.s1 = ss_;
+      ym.s2 = blk;
+      ym.s3 = 1;
+      ym.base = (int64_t)i * n_s * blk;
+      r = run_layer(x, (int64_t)B * tt, S, S, C, H, d, spatial, eps, r2, dtype, q, k, v, o, hb, false, s, ym, xm);
+      if (r != ST_OK) return r;
+    }
+    for (int j = 0; j < n_s; ++j) {
+      RowMap xm;   // slice row (b, e, i, a), t = i*tt + a -> hb row ((b*N_T + i)*N_S + j)*tt*ss + a*ss + e
+      xm.n1 = ss_;
+      xm.n2 = n_t;
+      xm.n3 = tt;
+      xm.s0 = TS;
+      xm.s1 = 1;
+      xm.s2 = (int64_t)n_s * blk;
+      xm.s3 = ss_;
+      xm.base = (int64_t)j * blk;
+      RowMap ym;   // slice row (b, e, t) -> y row (b*T + t)*S + j*ss + e
+      ym.n1 = ss_;
+      ym.n2 = T;
+      ym.s0 = TS;
+      ym.s1 = 1;
+      ym.s2 = S;
+      ym.base = (int64_t)j * ss_;
+      r = run_layer(hb, (int64_t)B * ss_, T, t_valid, C, H, d, temporal, eps, r1, dtype, q, k, v, o, y, true, s, ym,
+                    xm);
+      if (r != ST_OK) return r;
+    }
+    return ST_OK;
+  }
+
+  // Sliced schedule with explicit relayouts.  Blocked layout xb[b][i][j][a][e][c]
+  // with a < T/N_T, e < S/N_S.  Relayouts run on `side`, layers on `s`; with
+  // one stream this is the plain order of the pseudocode.
   Events E;
   if (side != s) {
     r = E.make(8);
@@ -240,7 +298,6 @@ st_status block_sliced(const void *x, int B, int T, int t_valid, int S, int grid
     r = order(s, side, E.ev[6]);   // the side stream starts after the caller's earlier work
     if (r != ST_OK) return r;
   }
-  const int tt = T / n_t, ss_ = S / n_s;
   const int64_t bstr[6] = {(int64_t)n_t * n_s * tt * ss_ * Cl, (int64_t)n_s * tt * ss_ * Cl, (int64_t)tt * ss_ * Cl,
                            ss_ * Cl, Cl, 1};   // strides of [B, N_T, N_S, tt, ss, C]
   void *xb = W + P.xb, *hb = W + P.hb;
@@ -382,7 +439,7 @@ st_status st_out_proj_relayout(const void *a, int64_t rows, int k_in, const void
   const size_t e = esize(dtype);
   const Range ry = rng(y, rows * n_out * e);
   if (overlap(ry, rng(a, rows * k_in * e)) || overlap(ry, rng(w, (int64_t)n_out * k_in * e))) return ST_EINVAL;
-  return do_linear(a, rows, k_in, w, n_out, dtype, y, (hipStream_t)stream, RowSwap{n1, n2});
+  return do_linear(a, rows, k_in, w, n_out, dtype, y, (hipStream_t)stream, row_swap(n1, n2));
 }
 
 static st_status attn_common(const void *q, const void *k, const void *v, int64_t outer, int L, int nv, int H, int d,

@@ -59,29 +59,41 @@ struct RopeArgs {
   int grid_w;
 };
 
-st_status launch_qkv_bf16(const void *x, int64_t rows, int c_in, const void *w, const float *g_q,
-                          const float *g_k, float eps, const RopeArgs &rope, int H, int d, void *q,
-                          void *k, void *v, hipStream_t s);
-// Output rows of a linear layer written in swapped order: rows in [outer, n1, n2]
-// order go to [outer, n2, n1]; n1 = 0 writes rows in place.
-struct RowSwap {
-  int64_t n1 = 0, n2 = 0;
+// Row map of a linear layer's input or output rows: row r, read as the
+// digits (r0, r1, r2, r3) of the mixed radix [*, n1, n2, n3] (r3 fastest),
+// goes to row base + r0*s0 + r1*s1 + r2*s2 + r3*s3.  n1 = 0 is the identity.
+struct RowMap {
+  int64_t n1 = 0, n2 = 1, n3 = 1;
+  int64_t s0 = 0, s1 = 0, s2 = 0, s3 = 0, base = 0;
 };
-__host__ __device__ inline int64_t swap_row(int64_t r, RowSwap sw) {
-  if (sw.n1 == 0) return r;
-  const int64_t blk = sw.n1 * sw.n2;
-  const int64_t o = r / blk, rem = r - o * blk;
-  const int64_t i = rem / sw.n2, j = rem - i * sw.n2;
-  return o * blk + j * sw.n1 + i;
+__host__ __device__ inline int64_t map_row(int64_t r, const RowMap &m) {
+  if (m.n1 == 0) return r;
+  const int64_t q3 = r / m.n3, d3 = r - q3 * m.n3;
+  const int64_t q2 = q3 / m.n2, d2 = q3 - q2 * m.n2;
+  const int64_t d0 = q2 / m.n1, d1 = q2 - d0 * m.n1;
+  return m.base + d0 * m.s0 + d1 * m.s1 + d2 * m.s2 + d3 * m.s3;
+}
+// Rows in [outer, n1, n2] order go to [outer, n2, n1].
+inline RowMap row_swap(int64_t n1, int64_t n2) {
+  RowMap m;
+  m.n1 = n1;
+  m.n2 = n2;
+  m.s0 = n1 * n2;
+  m.s1 = 1;
+  m.s2 = n1;
+  return m;
 }
 
+st_status launch_qkv_bf16(const void *x, int64_t rows, int c_in, const void *w, const float *g_q,
+                          const float *g_k, float eps, const RopeArgs &rope, int H, int d, void *q,
+                          void *k, void *v, hipStream_t s, RowMap xmap = {});
 st_status launch_linear_bf16(const void *a, int64_t rows, int k_in, const void *w, int n_out, void *y,
-                             hipStream_t s, RowSwap sw = {});
+                             hipStream_t s, RowMap ymap = {});
 st_status launch_qkv_f32(const float *x, int64_t rows, int c_in, const float *w, const float *g_q,
                          const float *g_k, float eps, const RopeArgs &rope, int H, int d, float *q,
                          float *k, float *v, hipStream_t s);
 st_status launch_linear_f32(const float *a, int64_t rows, int k_in, const float *w, int n_out, float *y,
-                            hipStream_t s, RowSwap sw = {});
+                            hipStream_t s, RowMap ymap = {});
 
 // Attention over the middle axis L of [outer, L, H, d] tensors, keys j >= n_valid masked.
 st_status launch_attn_bf16(const void *q, const void *k, const void *v, int64_t outer, int L, int n_valid,

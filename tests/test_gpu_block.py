@@ -46,18 +46,18 @@ def host_weights(w):
                 g_k=w["g_k"].astype(np.float64))
 
 
-def run_block(xd, wd, T, t_valid, S, grid_w, C, H, d, n_t, n_s, dt, two_streams=False):
+def run_block(xd, wd, T, t_valid, S, grid_w, C, H, d, n_t, n_s, dt, two_streams=False, B=1):
     sp = st.layer_weights(wd["s"]["w_qkv"], wd["s"]["w_o"], wd["s"]["g_q"], wd["s"]["g_k"])
     tp = st.layer_weights(wd["t"]["w_qkv"], wd["t"]["w_o"], wd["t"]["g_q"], wd["t"]["g_k"])
-    nbytes = st.st_block_sliced_workspace(1, T, S, grid_w, C, H, d, n_t, n_s, dt)
+    nbytes = st.st_block_sliced_workspace(B, T, S, grid_w, C, H, d, n_t, n_s, dt)
     ws = t_.empty(nbytes, dtype=t_.uint8, device="cuda")
-    y = empty((1, T, S, C), dt == st.ST_BF16)
+    y = empty((B, T, S, C), dt == st.ST_BF16)
     if two_streams:   # slice gathers/scatters on a second stream (default priority)
         side = t_.cuda.Stream()
-        st.st_block_sliced_2s(xd, 1, T, t_valid, S, grid_w, C, H, d, n_t, n_s, sp, tp, EPS, BASE, dt, y, ws, nbytes,
+        st.st_block_sliced_2s(xd, B, T, t_valid, S, grid_w, C, H, d, n_t, n_s, sp, tp, EPS, BASE, dt, y, ws, nbytes,
                               side_stream=side)
     else:
-        st.st_block_sliced(xd, 1, T, t_valid, S, grid_w, C, H, d, n_t, n_s, sp, tp, EPS, BASE, dt, y, ws, nbytes)
+        st.st_block_sliced(xd, B, T, t_valid, S, grid_w, C, H, d, n_t, n_s, sp, tp, EPS, BASE, dt, y, ws, nbytes)
     t_.cuda.synchronize()
     return y
 
@@ -151,6 +151,24 @@ def test_sliced_equals_unsliced_bf16(n_t, n_s):
     assert t_.equal(y1, ys)
     y2 = run_block(xd, wd, T, T, S, grid_w, C, H, d, n_t, n_s, st.ST_BF16, two_streams=True)
     assert t_.equal(y1, y2)
+
+
+def test_sliced_batch_of_two_equals_unsliced_and_oracle():
+    # B = 2: the row maps of the one-stream bf16 schedule carry a batch digit
+    B, T, S, grid_w, C, H, d = 2, 4, 24, 6, 1152, 16, 72
+    x1, w = small_inputs(9, T, S, C, H, d)
+    x2, _ = small_inputs(10, T, S, C, H, d)
+    x = np.concatenate([x1, x2], axis=0)
+    xd = to_dev(x)
+    wd = {k: dev_weights(v) for k, v in w.items()}
+    y1 = run_block(xd, wd, T, T, S, grid_w, C, H, d, 1, 1, st.ST_BF16, B=B)
+    ys = run_block(xd, wd, T, T, S, grid_w, C, H, d, 2, 3, st.ST_BF16, B=B)
+    assert t_.equal(y1, ys)
+    y2 = run_block(xd, wd, T, T, S, grid_w, C, H, d, 2, 3, st.ST_BF16, two_streams=True, B=B)
+    assert t_.equal(y1, y2)
+    wh = {k: host_weights(v) for k, v in w.items()}
+    y_ref = oracle.block_sliced(f64(x), wh["s"], wh["t"], H, d, grid_w, EPS, BASE, 2, 3)
+    assert_close(f64(ys), y_ref, True, "sliced block, B = 2")
 
 
 def test_padded_masked_schedule_equals_unpadded():
