@@ -244,6 +244,10 @@ def time_a2a_local(B, T, S, C, P, reps, stream):
         fn()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        # Each copy is shorter than a Python call through the binding, so the GPU is
+        # held busy while the host enqueues the timed calls: the events then time the
+        # kernels back to back, not the host's launch rate.
+        torch.cuda._sleep(20_000_000)
         e0.record(stream)
         for _ in range(reps):
             fn()

@@ -178,12 +178,26 @@ st_status launch_relayout(const void *src, const int64_t *src_str, void *dst, co
   const int64_t eb = elem_bytes;
   const bool inner_contig = SS.back() == 1 && DS.back() == 1;
   if (inner_contig && (int)D.size() < kMaxDims) {
-    // Few long rows (e.g. one contiguous block): split the row in halves until
-    // enough wavefronts share the copy.
+    // Few long rows (e.g. one contiguous block): cut every row into equal
+    // pieces of 2-8 KB so that enough wavefronts share the copy.  A piece is a
+    // whole number of 16-byte units when the row is, so cutting never narrows
+    // the vector width; failing an exact 2-8 KB divisor, rows are halved while
+    // the halves stay whole units of at least 2 KB.
     int64_t outer = 1;
     for (size_t k = 0; k + 1 < D.size(); ++k) outer *= D[k];
-    int64_t inner = D.back(), f = 1;
-    while (outer * f < 65536 && (inner / f) % 2 == 0 && (inner / f / 2) * eb >= 2048) f *= 2;
+    const int64_t inner = D.back(), row_bytes = inner * eb;
+    const int64_t grain = row_bytes % 16 == 0 ? 16 : eb;   // bytes; a multiple of eb
+    const int64_t units = row_bytes / grain;
+    int64_t f = 1;
+    if (outer < 65536 && row_bytes > 8192) {
+      for (int64_t pu = (2048 + grain - 1) / grain; pu * grain <= 8192; ++pu)
+        if (units % pu == 0) {
+          f = units / pu;
+          break;
+        }
+      if (f == 1)
+        while (outer * f < 65536 && (units / f) % 2 == 0 && (units / f / 2) * grain >= 2048) f *= 2;
+    }
     if (f > 1) {  // [..., inner] -> [..., f (stride inner/f), inner/f (stride 1)]
       const int64_t part = inner / f;
       D.back() = part;

@@ -103,6 +103,16 @@ def test_relayout_general_permutations(shape, perm, eb):
     assert np.array_equal(got.reshape(out_shape), np.transpose(src.reshape(shape), perm))
 
 
+# Few long rows, cut into 2-8 KB pieces: a contiguous block whose row count is not a power of two,
+# a pack-like permutation of long rows (the all-to-all pack of 8 ranks, scaled down), rows whose
+# byte length is not a multiple of 16 (left whole), and a row length with no 2-8 KB divisor.
+@pytest.mark.parametrize("shape,perm,eb", [((3 * 5 * 17 * 64 * 8,), (0,), 2), ((4, 3, 6, 2040), (1, 0, 2, 3), 2),
+                                           ((2, 3, 4099), (1, 0, 2), 4), ((2, 5, 3 * 4097), (1, 0, 2), 2),
+                                           ((3, 2062 * 8), (0, 1), 2)])   # no 2-8 KB divisor: halved once
+def test_relayout_long_rows(shape, perm, eb):
+    test_relayout_general_permutations(shape, perm, eb)
+
+
 def test_relayout_empty_is_noop():
     src = t_.zeros(16, dtype=t_.uint8, device="cuda")
     dst = t_.full((16,), 7, dtype=t_.uint8, device="cuda")
