@@ -123,8 +123,9 @@ def cpu_baseline(inp, cfg, budget_s=20.0):
 def time_slicing(x, wsd, wtd, B, T, S, gw, C, H, d, stream, reps):
     """The slicing schedule at one GPU: T padded with zero frames to a multiple of N_T, the
     spatial layer per time slice and the temporal layer per space slice (t_valid = T), on one
-    stream (st_block_sliced) and with the slice gathers/scatters on a second stream
-    (st_block_sliced_2s).  Headline N_T = N_S = 4 (T 52) plus the sweep N_T, N_S in {1,2,4,8}."""
+    stream (st_block_sliced: the rearranges, gathers and scatters ride on the projections' row
+    addressing) and with them as explicit copies on a second stream (st_block_sliced_2s).
+    Headline N_T = N_S = 4 (T 52) plus the sweep N_T, N_S in {1,2,4,8}."""
     import torch
 
     import st_synth

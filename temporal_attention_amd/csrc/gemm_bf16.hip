@@ -52,7 +52,7 @@ struct GemmArgs {
   int64_t M;
   int K, N;
   // plain output
-  u16 *y;            // [M, N], rows permuted by sw
+  u16 *y;            // [M, N]
   RowMap ymap;       // MODE 0: row r of the product is stored at row map_row(r, ymap) of y
   RowMap xmap;       // with XMAP: row r of the product reads row map_row(r, xmap) of x
   // qkv output
