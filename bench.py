@@ -18,7 +18,8 @@ same bytes, a
 roofline entry for the dominant kernel (spatial attention; its HBM traffic
 comes from the committed rocprofv3 counter summary when that summary matches
 the kernel source), the slicing schedule's time (N_T = N_S = 4, T padded to
-52), and the fp64 oracle timed on a bounded sample on the host cores.
+52), the spatial attention at the 4096 px image shape (3 heads x 128), and the
+fp64 oracle timed on a bounded sample on the host cores.
 """
 from __future__ import annotations
 
@@ -222,6 +223,34 @@ def time_v_change(lp, reps, stream):
             "ms_with_cache_refresh": round(ms_upd, 4)}
 
 
+def time_image_attention(reps, stream):
+    """Spatial attention at the 4096 px image shape (xDiT, "Experiments": image DiTs up to
+    4096 px): one sequence of 65,536 latent tokens, 3 heads x 128, seeded N(0, 1) q, k, v in
+    bf16; 4*S^2*d*H = 6.597 TFLOP per launch."""
+    import torch
+
+    import temporal_attention_amd as st
+
+    S, H, d = 65536, 3, 128
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4096)
+    q, k, v = (torch.randn((1, S, H, d), device="cuda", generator=g).to(torch.bfloat16) for _ in range(3))
+    o = torch.empty_like(q)
+    run = lambda: st.st_attn_spatial(q, k, v, 1, 1, S, H, d, 1.0 / math.sqrt(d), st.ST_BF16, o)  # noqa: E731
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = 4.0 * S * S * d * H
+    return {"workload": "4096px image DiT attention, 1 x 65536 tokens, 3 heads x 128", "ms": round(ms, 4),
+            "tflops": round(flops / ms / 1e9, 1), "frac_mfma_peak": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+
+
 def time_a2a_local(B, T, S, C, P, reps, stream):
     """One rank's local pack and unpack around the P-way all-to-all at the 1080p per-GPU shape
     (T padded to a multiple of P): each moves one rank's share, B*T*S*C/P elements, once."""
@@ -327,10 +356,11 @@ def main():
     ap.add_argument("--no-chunked", action="store_true", help="skip timing chunked attention + merges")
     ap.add_argument("--no-a2a", action="store_true", help="skip timing the all-to-all pack/unpack")
     ap.add_argument("--no-vchange", action="store_true", help="skip timing the V-Major change detection")
+    ap.add_argument("--no-image", action="store_true", help="skip timing attention at the 4096px image shape")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); multi-GPU runs are not part of this build",
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); it has no multi-GPU mode",
               file=sys.stderr)
         sys.exit(2)
 
@@ -482,6 +512,9 @@ def main():
 
     if not args.no_a2a:
         out["a2a_local"] = time_a2a_local(B, T, S, C, 8, max(3, args.steps), stream)
+
+    if not args.no_image:
+        out["attn_image_4096px"] = time_image_attention(max(3, args.steps // 2), stream)
 
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_budget)

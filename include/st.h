@@ -50,7 +50,7 @@ extern "C" {
 typedef enum {
   ST_OK = 0,
   ST_EINVAL = 1,        /* bad shape, NULL pointer, aliasing, unknown enum     */
-  ST_EUNSUPPORTED = 2,  /* valid request this build has no kernel for          */
+  ST_EUNSUPPORTED = 2,  /* valid request the library has no kernel for        */
   ST_EALIGN = 3,        /* pointer not aligned as required                     */
   ST_EWORKSPACE = 4,    /* workspace NULL or smaller than the query returned   */
   ST_ELAUNCH = 5        /* a HIP launch reported an error                      */

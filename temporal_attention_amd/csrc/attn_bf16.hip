@@ -64,6 +64,16 @@ struct Dims {
   // d, the ones row) fit in 16, they form one 16-row tile on the 16x16x32 MFMA.
   static constexpr bool PV16 = ONES && (D % 32) < 16;
   static constexpr int DT32 = PV16 ? D / 32 : DT;   // 32-row P.V tiles
+  // Long kernel, d = 64 or 128: K and V rows of 128 or 256 bytes would put
+  // chunk c of every row on the same LDS banks, so the 16-byte chunks of a
+  // row are stored permuted: physical chunk = logical chunk ^ swizzle(row).
+  // K: the 16 rows that one operand read visits at a logical chunk land on
+  // 16 different bank groups.  V (transpose reads, 4 rows x 64 bytes per
+  // read): the XOR moves whole 64-byte windows, so those rows differ there.
+  static constexpr bool SWZ = D % 64 == 0;
+  static constexpr int RPS = SWZ ? 128 / D : 1;   // rows per 256-byte bank span
+  __host__ __device__ static constexpr int kswz(int r) { return SWZ ? (r / RPS) % CH : 0; }
+  __host__ __device__ static constexpr int vswz(int r) { return SWZ ? 4 * ((r / RPS) % (CH / 4)) : 0; }
 };
 
 // Two LDS transpose reads, 8 keys apart, as one 8 x bf16 MFMA operand.
@@ -163,9 +173,12 @@ struct LongDma {
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int n = wave + C::WAVES * i;
-      const int b = n >= C::BLOCKS ? n - C::BLOCKS : n;
+      const bool isv = n >= C::BLOCKS;
+      const int b = isv ? n - C::BLOCKS : n;
       const int c = b * 64 + lane;
-      off[i] = (int)((c / Dims<D>::CH) * rs) + (c % Dims<D>::CH) * 8;
+      const int row = c / Dims<D>::CH, p = c % Dims<D>::CH;   // LDS row and physical chunk
+      const int chunk = p ^ (isv ? Dims<D>::vswz(row) : Dims<D>::kswz(row));
+      off[i] = (int)(row * rs) + chunk * 8;
     }
   }
 
@@ -223,6 +236,7 @@ struct LongWave {
   float lsum[NT];            // softmax denominator when V^T has no ones row
   float c;                   // scale * log2(e)
   int nv, l32, g, q16, v_off, v_off16;
+  int vsw;                   // SWZ: V chunk swizzle of this lane's rows, in 64-byte windows
   bool vkeep;                // lane's row of the last P.V tile is a real V^T row
   uint32_t vconst;           // otherwise its constant (ones row or zero)
 
@@ -232,7 +246,7 @@ struct LongWave {
     if constexpr (FOLD) kfix = u * 32 + l32 < nv ? kBf16One : (kBf16One | kBf16Big << 16);
 #pragma unroll
     for (int ks = 0; ks < DM::KS; ++ks) {
-      uint4 ku = *reinterpret_cast<const uint4 *>(Ks + l32 * D + ks * 16 + g * 8);
+      uint4 ku = *reinterpret_cast<const uint4 *>(Ks + l32 * D + ((ks * 2 + g) ^ DM::kswz(l32)) * 8);
       if constexpr (FOLD)
         if (ks == DM::KS - 1 && g) ku.x = kfix;
       kf[ks] = __builtin_bit_cast(bf16x8, ku);
@@ -344,7 +358,7 @@ struct LongWave {
       const u16 *vb = Vs + ks2 * 16 * D + v_off;
 #pragma unroll
       for (int dt = 0; dt < DM::DT32; ++dt) {
-        uint4 u = tr_read_pair<D>(vb + dt * 32);
+        uint4 u = tr_read_pair<D>(vb + (DM::SWZ ? dt ^ vsw : dt) * 32);
         if (!DM::PV16 && DM::DV != D && dt == DM::DT - 1 && !vkeep) u = make_uint4(vconst, vconst, vconst, vconst);
         const bf16x8 vf = __builtin_bit_cast(bf16x8, u);
 #pragma unroll
@@ -485,6 +499,9 @@ __global__ void __launch_bounds__(64 * kLongWaves, 8 / kLongWaves) attn_long_ker
   // of dimension dg + i: exactly the A-operand layout (row = lane % 32).
   const int grp = lane >> 4, gi = lane & 15;
   w.v_off = (gi >> 2) * D + 16 * (grp & 1) + 4 * (gi & 3) + 4 * (grp >> 1) * D;
+  // SWZ: the swizzle of key row (gi >> 2) + 4 (grp >> 1) (+ multiples of 8 for
+  // the other reads of the lane) is the same for all of them
+  w.vsw = DM::vswz((gi >> 2) + 4 * (grp >> 1)) / 4;
   // rows past D in the last P.V tile: the ones row, then zeros
   const int dlast = 32 * (DM::DT - 1) + w.l32;
   w.vkeep = dlast < D;
