@@ -236,7 +236,8 @@ struct LongWave {
   float lsum[NT];            // softmax denominator when V^T has no ones row
   float c;                   // scale * log2(e)
   int nv, l32, g, q16, v_off, v_off16;
-  int vsw;                   // SWZ: V chunk swizzle of this lane's rows, in 64-byte windows
+  int koff[DM::SWZ ? DM::KS : 1];     // SWZ: K operand offset of each 16-dim step within a unit's rows
+  int voff[DM::SWZ ? DM::DT32 : 1];   // SWZ: V^T read offset of each 32-row tile within a unit's rows
   bool vkeep;                // lane's row of the last P.V tile is a real V^T row
   uint32_t vconst;           // otherwise its constant (ones row or zero)
 
@@ -246,7 +247,11 @@ struct LongWave {
     if constexpr (FOLD) kfix = u * 32 + l32 < nv ? kBf16One : (kBf16One | kBf16Big << 16);
 #pragma unroll
     for (int ks = 0; ks < DM::KS; ++ks) {
-      uint4 ku = *reinterpret_cast<const uint4 *>(Ks + l32 * D + ((ks * 2 + g) ^ DM::kswz(l32)) * 8);
+      uint4 ku;
+      if constexpr (DM::SWZ)
+        ku = *reinterpret_cast<const uint4 *>(Ks + koff[ks]);
+      else
+        ku = *reinterpret_cast<const uint4 *>(Ks + l32 * D + ks * 16 + g * 8);
       if constexpr (FOLD)
         if (ks == DM::KS - 1 && g) ku.x = kfix;
       kf[ks] = __builtin_bit_cast(bf16x8, ku);
@@ -358,7 +363,7 @@ struct LongWave {
       const u16 *vb = Vs + ks2 * 16 * D + v_off;
 #pragma unroll
       for (int dt = 0; dt < DM::DT32; ++dt) {
-        uint4 u = tr_read_pair<D>(vb + (DM::SWZ ? dt ^ vsw : dt) * 32);
+        uint4 u = tr_read_pair<D>(DM::SWZ ? Vs + ks2 * 16 * D + voff[dt] : vb + dt * 32);
         if (!DM::PV16 && DM::DV != D && dt == DM::DT - 1 && !vkeep) u = make_uint4(vconst, vconst, vconst, vconst);
         const bf16x8 vf = __builtin_bit_cast(bf16x8, u);
 #pragma unroll
@@ -499,9 +504,16 @@ __global__ void __launch_bounds__(64 * kLongWaves, 8 / kLongWaves) attn_long_ker
   // of dimension dg + i: exactly the A-operand layout (row = lane % 32).
   const int grp = lane >> 4, gi = lane & 15;
   w.v_off = (gi >> 2) * D + 16 * (grp & 1) + 4 * (gi & 3) + 4 * (grp >> 1) * D;
-  // SWZ: the swizzle of key row (gi >> 2) + 4 (grp >> 1) (+ multiples of 8 for
-  // the other reads of the lane) is the same for all of them
-  w.vsw = DM::vswz((gi >> 2) + 4 * (grp >> 1)) / 4;
+  if constexpr (DM::SWZ) {
+    // Swizzled rows (see Dims): the XORs are per lane and per step, so the
+    // offsets are computed once.  A lane's V rows are (gi >> 2) + 4 (grp >> 1)
+    // plus multiples of 8, which all share one swizzle.
+    const int vsw = DM::vswz((gi >> 2) + 4 * (grp >> 1)) / 4;
+#pragma unroll
+    for (int ks = 0; ks < DM::KS; ++ks) w.koff[ks] = w.l32 * D + ((ks * 2 + w.g) ^ DM::kswz(w.l32)) * 8;
+#pragma unroll
+    for (int dt = 0; dt < DM::DT32; ++dt) w.voff[dt] = w.v_off + (dt ^ vsw) * 32;
+  }
   // rows past D in the last P.V tile: the ones row, then zeros
   const int dlast = 32 * (DM::DT - 1) + w.l32;
   w.vkeep = dlast < D;
