@@ -92,24 +92,46 @@ st_status st_rope_table(int d, int kind, float base, int n_pos, float *table, vo
  *   w_qkv    in   [3*H*d, c_in]          (dtype)
  *   g_q,g_k  in   fp32 [d]               RMSNorm gains, shared by the heads
  *   eps           RMSNorm epsilon: t_j * g_j / sqrt(mean_j t_j^2 + eps), per (row, head)
- *   rope_kind     st_rope_kind.  ST_ROPE_NONE ignores the four arguments below.
- *   rope_table in fp32 table from st_rope_table() for the same d and kind
- *   rope_npos     positions in the table; every position used must be < rope_npos
+ *   q_scale       > 0: q is stored multiplied by q_scale (1: plain q).  A layer that
+ *                 passes (1/sqrt(d)) * log2(e) here and calls the attention with
+ *                 scale = ln 2 computes the same softmax with q rounded once, here;
+ *                 st_layer_scales() returns the pair the layer pair uses.
+ *   rope_kind     st_rope_kind.  ST_ROPE_NONE ignores the arguments below up to H.
+ *   rope_table in fp32 table from st_rope_table() (for the same d, kind and base)
+ *   rope_npos     positions in the table
+ *   pos      in   int32 [rows, 2], 8-byte aligned, or NULL.  Non-NULL: the position of
+ *                 row r is pos[r] = (t, unused) for 1D, (h, w) for 2D -- any position set,
+ *                 each value in [0, rope_npos) (values outside are clamped into the
+ *                 table; the result is then unspecified, never a fault).
  *   pos_period, pos_offset, grid_w
- *                 position of row r: i = r % pos_period + pos_offset;
- *                 1D: p = i;  2D: h = i / grid_w, w = i % grid_w.
- *                 Rows in [.., S] order with pos_period = S give a frame's
- *                 patches; rows in [.., T] order with pos_period = T give frames.
+ *                 used when pos is NULL: position of row r: i = r % pos_period + pos_offset;
+ *                 1D: p = i;  2D: h = i / grid_w, w = i % grid_w.  Rows in [.., S] order
+ *                 with pos_period = S give a frame's patches; rows in [.., T] order with
+ *                 pos_period = T give frames.  Every position must be < rope_npos (ST_EINVAL).
  *   H, d          heads and head dim; dtype ST_BF16 supports d in {64, 72, 128},
  *                 ST_F32 supports even d <= 128 (multiple of 4 for 2D RoPE).
- *   q, k, v  out  [rows, H, d]           (dtype)
+ *   q, k, v  out  [rows, H, d]           (dtype); must not overlap x, w_qkv, pos or each other
  * bf16: c_in must be a multiple of 64 (the K step of the MFMA pipeline).  rows may be 0 (no work).
  */
 st_status st_qkv_norm_rope(const void *x, int64_t rows, int c_in, const void *w_qkv,
-                           const float *g_q, const float *g_k, float eps,
-                           int rope_kind, const float *rope_table, int rope_npos,
+                           const float *g_q, const float *g_k, float eps, float q_scale,
+                           int rope_kind, const float *rope_table, int rope_npos, const int32_t *pos,
                            int64_t pos_period, int64_t pos_offset, int grid_w,
                            int H, int d, int dtype, void *q, void *k, void *v, void *stream);
+
+/*
+ * st_layer_scales -- the q scale and attention scale a layer of st_block_sliced
+ * uses for head dim d (host call, no GPU work).  The attention is
+ * softmax(q.k / sqrt(d)) either way (ScaleFusion review, "Technical
+ * architecture": the layers are attention layers of the transformer):
+ *   ST_BF16: q_scale = (1/sqrt(d)) * log2(e), attn_scale = ln 2 -- q is stored
+ *            pre-scaled, so the attention kernel's base-2 exponent is the
+ *            score itself and needs no multiply;
+ *   ST_F32:  q_scale = 1, attn_scale = 1/sqrt(d).
+ * q_scale, attn_scale: host pointers to one float each.  ST_EINVAL for d < 1,
+ * an unknown dtype or a NULL pointer.
+ */
+st_status st_layer_scales(int d, int dtype, float *q_scale, float *attn_scale);
 
 /*
  * st_out_proj -- output projection of the attention result: y = a . w^T.

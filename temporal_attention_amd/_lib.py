@@ -22,7 +22,7 @@ ST_ROPE_NONE, ST_ROPE_1D, ST_ROPE_2D = 0, 1, 2
 
 # Every entry point declared in include/st.h.
 EXPORTS = (
-    "st_status_str", "st_rope_table_floats", "st_rope_table", "st_qkv_norm_rope", "st_out_proj",
+    "st_status_str", "st_rope_table_floats", "st_rope_table", "st_qkv_norm_rope", "st_layer_scales", "st_out_proj",
     "st_out_proj_relayout", "st_attn_spatial", "st_attn_temporal", "st_attn_chunk", "st_attn_chunk_acc",
     "st_attn_merge", "st_relayout", "st_block_sliced", "st_block_sliced_2s", "st_block_sliced_workspace",
     "st_v_change",
@@ -57,8 +57,9 @@ _SIGS = {
     "st_status_str": (C.c_char_p, [_i]),
     "st_rope_table_floats": (_sz, [_i, _i, _i]),
     "st_rope_table": (_i, [_i, _i, _f, _i, _p, _p]),
-    "st_qkv_norm_rope": (_i, [_p, _i64, _i, _p, _p, _p, _f, _i, _p, _i, _i64, _i64, _i, _i, _i, _i, _p, _p, _p,
-                              _p]),
+    "st_qkv_norm_rope": (_i, [_p, _i64, _i, _p, _p, _p, _f, _f, _i, _p, _i, _p, _i64, _i64, _i, _i, _i, _i, _p, _p,
+                              _p, _p]),
+    "st_layer_scales": (_i, [_i, _i, C.POINTER(C.c_float), C.POINTER(C.c_float)]),
     "st_out_proj": (_i, [_p, _i64, _i, _p, _i, _i, _p, _p]),
     "st_out_proj_relayout": (_i, [_p, _i64, _i, _p, _i, _i, _i64, _i64, _p, _p]),
     "st_attn_spatial": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p, _p]),
@@ -119,11 +120,18 @@ def st_rope_table(d, kind, base, n_pos, table, stream=None):
     _check("st_rope_table", lib.st_rope_table(d, kind, base, n_pos, _ptr(table), _stream(stream)))
 
 
-def st_qkv_norm_rope(x, rows, c_in, w_qkv, g_q, g_k, eps, rope_kind, rope_table, rope_npos, pos_period, pos_offset,
-                     grid_w, H, d, dtype, q, k, v, stream=None):
+def st_qkv_norm_rope(x, rows, c_in, w_qkv, g_q, g_k, eps, q_scale, rope_kind, rope_table, rope_npos, pos, pos_period,
+                     pos_offset, grid_w, H, d, dtype, q, k, v, stream=None):
     _check("st_qkv_norm_rope", lib.st_qkv_norm_rope(
-        _ptr(x), rows, c_in, _ptr(w_qkv), _ptr(g_q), _ptr(g_k), eps, rope_kind, _ptr(rope_table), rope_npos,
-        pos_period, pos_offset, grid_w, H, d, dtype, _ptr(q), _ptr(k), _ptr(v), _stream(stream)))
+        _ptr(x), rows, c_in, _ptr(w_qkv), _ptr(g_q), _ptr(g_k), eps, q_scale, rope_kind, _ptr(rope_table), rope_npos,
+        _ptr(pos), pos_period, pos_offset, grid_w, H, d, dtype, _ptr(q), _ptr(k), _ptr(v), _stream(stream)))
+
+
+def st_layer_scales(d, dtype):
+    """(q_scale, attn_scale) of a layer of st_block_sliced for head dim d."""
+    qs, at = C.c_float(), C.c_float()
+    _check("st_layer_scales", lib.st_layer_scales(d, dtype, C.byref(qs), C.byref(at)))
+    return qs.value, at.value
 
 
 def st_out_proj(a, rows, k_in, w, n_out, dtype, y, stream=None):

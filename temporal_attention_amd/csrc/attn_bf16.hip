@@ -119,16 +119,11 @@ constexpr float kRescale = 8.0f;   // log2 growth of the running max that forces
 // Keys per LDS tile of the long kernel for d <= 72: one workgroup barrier per
 // tile, so larger tiles mean fewer barriers (d = 128 keeps 64 keys so three
 // stages fit in LDS).
-#ifndef ST_KB
-#define ST_KB 128
-#endif
-#ifndef ST_LONG_WAVES
-#define ST_LONG_WAVES 8
-#endif
+constexpr int kLongKeys = 128;
 // Waves per workgroup of the long kernel: every workgroup streams all keys of
 // its sequence through LDS, so more queries per workgroup means less L2->LDS
 // traffic per flop.
-constexpr int kLongWaves = ST_LONG_WAVES;
+constexpr int kLongWaves = 8;
 
 // ------------------------------------------------------------------------- //
 // Long sequences                                                            //
@@ -137,7 +132,7 @@ template <int D, int NT, int W = kLongWaves>
 struct LongCfg {
   typedef Dims<D> DM;
   static constexpr int WAVES = W;                 // waves per workgroup
-  static constexpr int KB = D <= 72 ? ST_KB : 64;  // keys per LDS tile
+  static constexpr int KB = D <= 72 ? kLongKeys : 64;  // keys per LDS tile
   static constexpr int QW = 32 * NT;              // queries per wave
   static constexpr int QB = WAVES * QW;           // queries per workgroup
   static constexpr int TILE = KB * D;             // u16 per K or V tile: rows packed as in memory
@@ -212,17 +207,24 @@ struct LongDma {
 // independent, so the MFMA pipe and the vector ALU stay busy together.
 //
 // d = 72 (FOLD): the Q.K contraction is padded to 80 dimensions, and two of
-// the spare ones carry the softmax bookkeeping into the MFMA.  Q is
-// pre-multiplied by scale * log2(e); Q dim 72 holds -m (the running max in
-// those units, kept bf16-exact) against K dim 72 = 1, and Q dim 73 holds -1
-// against K dim 73 = 0 for a valid key or 2^120 for a masked one.  The
-// accumulator then is already c*s - m (or about -2^120), so a probability is
-// one exp2 and masking costs nothing in the loop.
+// the spare ones carry the softmax bookkeeping into the MFMA.  Q dim 72 holds
+// -m (the running max, kept bf16-exact) against K dim 72 = 1, and Q dim 73
+// holds -1 against K dim 73 = 0 for a valid key or 2^120 for a masked one, so
+// the accumulator is already the score minus the max (or about -2^120), and
+// masking costs nothing in the loop.
+//   PRE (c = scale * log2(e) a power of two): Q is multiplied by c exactly, so
+//   the accumulator is the exp2 argument itself and a probability is one exp2.
+//   The layer pair stores q already multiplied by scale * log2(e) (a gain of
+//   its RMSNorm epilogue, rounded to bf16 once) and attends with c = 1.
+//   Otherwise Q enters the contraction as stored and the exponent is c * acc:
+//   one multiply more per score.  Rounding c * Q to bf16 in the kernel instead
+//   would add a second rounding of up to 2^-8 relative to every element, which
+//   peaked softmaxes turn into output errors of several 1e-2.
 constexpr uint32_t kBf16One = 0x3F80u, kBf16NegOne = 0xBF80u, kBf16Big = 0x7B80u;   // 1, -1, 2^120
 
 __device__ __forceinline__ float round_bf16(float x) { return __uint_as_float(pack_bf16x2(x, 0.f) << 16); }
 
-template <int D, int NT>
+template <int D, int NT, bool PRE>
 struct LongWave {
   typedef LongCfg<D, NT> C;
   typedef Dims<D> DM;
@@ -232,9 +234,10 @@ struct LongWave {
   bf16x8 qf[NT][DM::KS];     // Q^T operand (B of S^T = K Q^T)
   f32x16 oacc[DM::DT32][NT]; // O^T accumulator, 32-row tiles
   f32x4 oacc16[NT][2];       // PV16: last 16 rows of O^T, queries 0..15 and 16..31 of a tile
-  float m[NT];               // running max: FOLD, scaled log2 units; else raw scores
+  float m[NT];               // running max (FOLD: in accumulator units, bf16-exact; else raw scores)
   float lsum[NT];            // softmax denominator when V^T has no ones row
   float c;                   // scale * log2(e)
+  float thr;                 // FOLD: the rescale threshold in accumulator units (kRescale, or kRescale / c)
   int nv, l32, g, q16, v_off, v_off16;
   int koff[DM::SWZ ? DM::KS : 1];     // SWZ: K operand offset of each 16-dim step within a unit's rows
   int voff[DM::SWZ ? DM::DT32 : 1];   // SWZ: V^T read offset of each 32-row tile within a unit's rows
@@ -290,7 +293,7 @@ struct LongWave {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       lm[nt] = max16(s[nt]);
-      if constexpr (FOLD) grow |= lm[nt] > kRescale;
+      if constexpr (FOLD) grow |= lm[nt] > thr;
       else grow |= (lm[nt] - m[nt]) * c > kRescale;
     }
     return __builtin_amdgcn_ballot_w64(grow) != 0;
@@ -302,10 +305,10 @@ struct LongWave {
     for (int nt = 0; nt < NT; ++nt) {
       const float mx = max_across_halves(lm[nt]);
       if constexpr (FOLD) {
-        // s holds c*score - m; the new max is bf16-exact so -m fits Q dim 72.
+        // s holds (scaled) score - m; the new max is bf16-exact so -m fits Q dim 72.
         const float mnew = round_bf16(m[nt] + (first ? mx : fmaxf(mx, 0.f)));
         const float delta = mnew - m[nt];
-        if (!first) scale_acc(nt, __builtin_amdgcn_exp2f(-delta));
+        if (!first) scale_acc(nt, __builtin_amdgcn_exp2f(PRE ? -delta : -delta * c));
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[nt][r] -= delta;
         m[nt] = mnew;
@@ -340,7 +343,7 @@ struct LongWave {
   __device__ __forceinline__ void probs(f32x16 &s, bf16x8 (&pf)[2][NT], int nt) {
     if constexpr (FOLD) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(s[r]);
+      for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(PRE ? s[r] : s[r] * c);
     } else {
       const float mc = m[nt] * c;
 #pragma unroll
@@ -424,12 +427,12 @@ struct LongWave {
   }
 };
 
-template <int D, int NT>
+template <int D, int NT, bool PRE>
 __global__ void __launch_bounds__(64 * kLongWaves, 8 / kLongWaves) attn_long_kernel(AttnArgs a, uint32_t nqb,
                                                                                   uint32_t nblocks) {
   typedef LongCfg<D, NT> C;
   typedef Dims<D> DM;
-  typedef LongWave<D, NT> W;
+  typedef LongWave<D, NT, PRE> W;
   __shared__ __attribute__((aligned(16))) u16 lds[C::NSTAGE * C::STAGE];
 
   const uint32_t tile = xcd_remap(blockIdx.x, nblocks);
@@ -449,6 +452,7 @@ __global__ void __launch_bounds__(64 * kLongWaves, 8 / kLongWaves) attn_long_ker
 
   W w;
   w.c = a.c;
+  w.thr = PRE ? kRescale : kRescale / a.c;
   w.nv = min(Lk, a.n_valid);
   w.l32 = lane & 31;
   w.g = lane >> 5;
@@ -459,8 +463,8 @@ __global__ void __launch_bounds__(64 * kLongWaves, 8 / kLongWaves) attn_long_ker
   for (int i = t; i < 2 * C::NSTAGE * C::SLACK; i += 64 * C::WAVES)
     lds[(i / C::SLACK) * C::REGION + C::TILE + i % C::SLACK] = 0;
 
-  // Q operand fragments, held for the whole key loop (FOLD: times c, plus
-  // the -m and -1 terms; m starts at 0).
+  // Q operand fragments, held for the whole key loop (FOLD: PRE multiplies
+  // by c, exactly; the -m and -1 terms in dims 72 and 73, m starts at 0).
   const int q0 = qb * C::QB + wave * C::QW;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
@@ -470,14 +474,15 @@ __global__ void __launch_bounds__(64 * kLongWaves, 8 / kLongWaves) attn_long_ker
       const int dd = ks * 16 + w.g * 8;
       uint4 u = make_uint4(0, 0, 0, 0);
       if (qi < L && dd < D) u = *reinterpret_cast<const uint4 *>(qp + (int64_t)qi * rs + dd);
-      if constexpr (W::FOLD) {
+      if constexpr (W::FOLD && PRE) {
         uint32_t x[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           x[j] = pack_bf16x2(__uint_as_float(x[j] << 16) * w.c, __uint_as_float(x[j] & 0xFFFF0000u) * w.c);
         u = make_uint4(x[0], x[1], x[2], x[3]);
-        if (ks == DM::KS - 1 && w.g) u.x = kBf16NegOne << 16;
       }
+      if constexpr (W::FOLD)
+        if (ks == DM::KS - 1 && w.g) u.x = kBf16NegOne << 16;
       w.qf[nt][ks] = __builtin_bit_cast(bf16x8, u);
     }
   }
@@ -609,7 +614,7 @@ __global__ void __launch_bounds__(64 * kLongWaves, 8 / kLongWaves) attn_long_ker
     float fa = 0.f, fp = 1.f;
     if (a.lse) {
       // sum_j exp(scale s_j) = 2^M * l, M = the running max in scaled log2 units
-      const float M = W::FOLD ? w.m[nt] : w.m[nt] * w.c;
+      const float M = (W::FOLD && PRE) ? w.m[nt] : w.m[nt] * w.c;
       float lse = (M + log2f(l)) * 0.69314718055994531f;
       const int64_t li = (outer * a.H + h) * (int64_t)L + qi;
       if (a.acc) {
@@ -877,13 +882,13 @@ attn_short_kernel(AttnArgs a, uint32_t nblocks) {
   }
 }
 
-template <int D, int NT>
+template <int D, int NT, bool PRE = false>
 st_status launch_long(const AttnArgs &a, hipStream_t s) {
   typedef LongCfg<D, NT> C;
   const int64_t nqb = (a.L + C::QB - 1) / C::QB;
   const int64_t nb = nqb * a.outer * a.H;
   if (nb >= (1ll << 31)) return ST_EUNSUPPORTED;
-  hipLaunchKernelGGL((attn_long_kernel<D, NT>), dim3((uint32_t)nb), dim3(64 * C::WAVES), 0, s, a, (uint32_t)nqb,
+  hipLaunchKernelGGL((attn_long_kernel<D, NT, PRE>), dim3((uint32_t)nb), dim3(64 * C::WAVES), 0, s, a, (uint32_t)nqb,
                      (uint32_t)nb);
   return launch_status();
 }
@@ -894,6 +899,12 @@ st_status launch_short(const AttnArgs &a, hipStream_t s) {
   if (nb >= (1ll << 31)) return ST_EUNSUPPORTED;
   hipLaunchKernelGGL((attn_short_kernel<D, NT>), dim3((uint32_t)nb), dim3(256), 0, s, a, (uint32_t)nb);
   return launch_status();
+}
+
+// c is a power of two: multiplying bf16 values by it is exact (no overflow at attention scales).
+bool pow2(float c) {
+  int e;
+  return c > 0.f && frexpf(c, &e) == 0.5f && e > -100 && e < 100;
 }
 
 AttnArgs make_args(const void *q, const void *k, const void *v, int64_t outer, int L, int Lk, int n_valid, int H,
@@ -930,7 +941,7 @@ st_status launch_attn_chunk_bf16(const void *q, const void *k, const void *v, in
   if (outer == 0 || Lq == 0) return ST_OK;
   const AttnArgs a = make_args(q, k, v, outer, Lq, Lk, n_valid, H, scale, out, lse, accumulate);
   switch (d) {
-    case 72: return launch_long<72, 2>(a, s);
+    case 72: return pow2(a.c) ? launch_long<72, 2, true>(a, s) : launch_long<72, 2, false>(a, s);
     case 64: return launch_long<64, 2>(a, s);
     case 128: return launch_long<128, 1>(a, s);
     default: return ST_EUNSUPPORTED;

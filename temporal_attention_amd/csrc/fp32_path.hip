@@ -41,7 +41,7 @@ __global__ void qkv_f32_kernel(const float *x, int64_t rows, int K, const float 
 
 // In place on q and k: RMSNorm over d, then RoPE.  One thread per (row, head, tensor).
 __global__ void norm_rope_f32_kernel(int64_t rows, int H, int d, float *q, float *k, const float *g_q,
-                                     const float *g_k, float eps, RopeArgs rope) {
+                                     const float *g_k, float eps, float q_scale, RopeArgs rope) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= rows * H * 2) return;
   const int which = (int)(i % 2);
@@ -52,15 +52,21 @@ __global__ void norm_rope_f32_kernel(int64_t rows, int H, int d, float *q, float
   float ss = 0.f;
   for (int j = 0; j < d; ++j) ss = fmaf(t[j], t[j], ss);
   const float inv = rsqrtf(ss / (float)d + eps);
-  for (int j = 0; j < d; ++j) t[j] = t[j] * inv * g[j];
+  const float qs = which == 0 ? q_scale : 1.0f;
+  for (int j = 0; j < d; ++j) t[j] = t[j] * inv * (g[j] * qs);
   if (rope.kind == ST_ROPE_NONE) return;
-  const int64_t pi = r % rope.period + rope.offset;
   int p0, p1 = 0;
-  if (rope.kind == ST_ROPE_1D) {
-    p0 = (int)pi;
+  if (rope.pos) {   // caller's positions, clamped into the table
+    p0 = min(max(rope.pos[2 * r], 0), rope.npos - 1);
+    p1 = min(max(rope.pos[2 * r + 1], 0), rope.npos - 1);
   } else {
-    p0 = (int)(pi / rope.grid_w);
-    p1 = (int)(pi % rope.grid_w);
+    const int64_t pi = r % rope.period + rope.offset;
+    if (rope.kind == ST_ROPE_1D) {
+      p0 = (int)pi;
+    } else {
+      p0 = (int)(pi / rope.grid_w);
+      p1 = (int)(pi % rope.grid_w);
+    }
   }
   const int npairs = rope.kind == ST_ROPE_2D ? d / 4 : d / 2;
   for (int j = 0; j < d; j += 2) {
@@ -133,14 +139,14 @@ inline unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
 }  // namespace
 
 st_status launch_qkv_f32(const float *x, int64_t rows, int c_in, const float *w, const float *g_q,
-                         const float *g_k, float eps, const RopeArgs &rope, int H, int d, float *q, float *k,
-                         float *v, hipStream_t s) {
+                         const float *g_k, float eps, float q_scale, const RopeArgs &rope, int H, int d, float *q,
+                         float *k, float *v, hipStream_t s) {
   if (rows == 0) return ST_OK;
   const int64_t n = rows * 3 * H * d;
   if (blocks_for(n) >= (1u << 31) || blocks_for(rows * H * 2) >= (1u << 31)) return ST_EUNSUPPORTED;
   hipLaunchKernelGGL(qkv_f32_kernel, dim3(blocks_for(n)), dim3(256), 0, s, x, rows, c_in, w, H, d, q, k, v);
   hipLaunchKernelGGL(norm_rope_f32_kernel, dim3(blocks_for(rows * H * 2)), dim3(256), 0, s, rows, H, d, q, k, g_q,
-                     g_k, eps, rope);
+                     g_k, eps, q_scale, rope);
   return launch_status();
 }
 

@@ -60,6 +60,7 @@ struct GemmArgs {
   int H;
   const float *g_q, *g_k;
   float eps;
+  float q_scale;     // q is stored times q_scale
   RopeArgs rope;
 };
 
@@ -318,12 +319,18 @@ __device__ __forceinline__ void epilogue_qkv(const GemmArgs &a, f32x4 (&acc)[CT]
     roff[tt] = r < a.M ? r * hd : -1;
     p0[tt] = p1[tt] = 0;
     if (a.rope.kind != ST_ROPE_NONE) {
-      const uint32_t i = (base_i + (uint32_t)(wm * kWM + tt * 16 + l16)) % period + (uint32_t)a.rope.offset;
-      if (a.rope.kind == ST_ROPE_1D) {
-        p0[tt] = (int)i;
+      if (a.rope.pos) {   // caller's positions, clamped into the table (out-of-range positions are undefined)
+        const int2 pp = *reinterpret_cast<const int2 *>(a.rope.pos + 2 * min<int64_t>(r, a.M - 1));
+        p0[tt] = min(max(pp.x, 0), a.rope.npos - 1);
+        p1[tt] = min(max(pp.y, 0), a.rope.npos - 1);
       } else {
-        p0[tt] = (int)(i / (uint32_t)a.rope.grid_w);
-        p1[tt] = (int)(i - (uint32_t)p0[tt] * (uint32_t)a.rope.grid_w);
+        const uint32_t i = (base_i + (uint32_t)(wm * kWM + tt * 16 + l16)) % period + (uint32_t)a.rope.offset;
+        if (a.rope.kind == ST_ROPE_1D) {
+          p0[tt] = (int)i;
+        } else {
+          p0[tt] = (int)(i / (uint32_t)a.rope.grid_w);
+          p1[tt] = (int)(i - (uint32_t)p0[tt] * (uint32_t)a.rope.grid_w);
+        }
       }
     }
   }
@@ -344,7 +351,8 @@ __device__ __forceinline__ void epilogue_qkv(const GemmArgs &a, f32x4 (&acc)[CT]
       const int which = gh / H;              // 0 q, 1 k, 2 v
       const int jd = cl - hh * D;            // dim within the head (multiple of 4)
       const bool norm = !GENERAL || which < 2;
-      const float4 g = *reinterpret_cast<const float4 *>((which == 0 ? a.g_q : a.g_k) + jd);
+      float4 g = *reinterpret_cast<const float4 *>((which == 0 ? a.g_q : a.g_k) + jd);
+      if (which == 0) g = make_float4(g.x * a.q_scale, g.y * a.q_scale, g.z * a.q_scale, g.w * a.q_scale);
       const bool second = a.rope.kind == ST_ROPE_2D && jd >= D / 2;
       const int pair = (jd - (second ? D / 2 : 0)) >> 1;
       u16 *dst = (which == 0 ? a.q : (which == 1 ? a.k : a.v)) + (gh - which * H) * D + jd;
@@ -396,8 +404,8 @@ st_status launch_gemm(const GemmArgs &a, hipStream_t s) {
 }  // namespace
 
 st_status launch_qkv_bf16(const void *x, int64_t rows, int c_in, const void *w, const float *g_q, const float *g_k,
-                          float eps, const RopeArgs &rope, int H, int d, void *q, void *k, void *v, hipStream_t s,
-                          RowMap xmap) {
+                          float eps, float q_scale, const RopeArgs &rope, int H, int d, void *q, void *k, void *v,
+                          hipStream_t s, RowMap xmap) {
   GemmArgs a{};
   a.x = static_cast<const u16 *>(x);
   a.w = static_cast<const u16 *>(w);
@@ -411,6 +419,7 @@ st_status launch_qkv_bf16(const void *x, int64_t rows, int c_in, const void *w, 
   a.g_q = g_q;
   a.g_k = g_k;
   a.eps = eps;
+  a.q_scale = q_scale;
   a.rope = rope;
   a.xmap = xmap;
   const bool mapped = xmap.n1 != 0;

@@ -28,12 +28,15 @@ bool head_dim_ok(int d, int dt, int rope_kind) {
   return true;
 }
 
-st_status check_rope(int kind, const float *table, int npos, int64_t period, int64_t offset, int grid_w, int d,
-                     int64_t rows) {
+st_status check_rope(int kind, const float *table, int npos, const int32_t *pos, int64_t period, int64_t offset,
+                     int grid_w, int d, int64_t rows) {
   if (kind == ST_ROPE_NONE) return ST_OK;
   if (kind != ST_ROPE_1D && kind != ST_ROPE_2D) return ST_EINVAL;
-  if (!table || npos < 1 || period < 1 || offset < 0) return ST_EINVAL;
+  if (!table || npos < 1) return ST_EINVAL;
   if (!aligned16(table)) return ST_EALIGN;
+  if (kind == ST_ROPE_2D && d % 4) return ST_EINVAL;
+  if (pos) return (uintptr_t)pos % 8 ? ST_EALIGN : ST_OK;   // positions are device data: range is the caller's
+  if (period < 1 || offset < 0) return ST_EINVAL;
   const int64_t imax = std::min<int64_t>(period, std::max<int64_t>(rows, 1)) - 1 + offset;   // largest index used
   if (kind == ST_ROPE_1D) return imax < npos ? ST_OK : ST_EINVAL;
   if (grid_w < 1 || d % 4) return ST_EINVAL;
@@ -44,11 +47,11 @@ st_status check_rope(int kind, const float *table, int npos, int64_t period, int
 // ---------------------------------------------------------------- dispatch
 // xmap (bf16 only): row r of the projection reads row map_row(r, xmap) of x.
 st_status do_qkv(const void *x, int64_t rows, int c_in, const void *w, const float *gq, const float *gk, float eps,
-                 const RopeArgs &rope, int H, int d, int dt, void *q, void *k, void *v, hipStream_t s,
+                 float q_scale, const RopeArgs &rope, int H, int d, int dt, void *q, void *k, void *v, hipStream_t s,
                  RowMap xmap = {}) {
-  if (dt == ST_BF16) return launch_qkv_bf16(x, rows, c_in, w, gq, gk, eps, rope, H, d, q, k, v, s, xmap);
+  if (dt == ST_BF16) return launch_qkv_bf16(x, rows, c_in, w, gq, gk, eps, q_scale, rope, H, d, q, k, v, s, xmap);
   if (xmap.n1 != 0) return ST_EUNSUPPORTED;
-  return launch_qkv_f32((const float *)x, rows, c_in, (const float *)w, gq, gk, eps, rope, H, d, (float *)q,
+  return launch_qkv_f32((const float *)x, rows, c_in, (const float *)w, gq, gk, eps, q_scale, rope, H, d, (float *)q,
                         (float *)k, (float *)v, s);
 }
 
@@ -74,7 +77,12 @@ struct BlockPlan {
   int npos2, npos1;
 };
 
-BlockPlan plan_block(int B, int T, int S, int grid_w, int C, int H, int d, int n_t, int n_s, int dt) {
+// explicit_copies: the sliced schedule moves slices with relayout passes (fp32, or
+// the two-stream variant) and needs the blocked buffers and double-buffered
+// slice buffers; the one-stream bf16 schedule needs only the blocked
+// intermediate hb and the per-slice q, k, v, o.
+BlockPlan plan_block(int B, int T, int S, int grid_w, int C, int H, int d, int n_t, int n_s, int dt,
+                     bool explicit_copies) {
   BlockPlan p{};
   const size_t e = esize(dt);
   const int64_t N = (int64_t)B * T * S;
@@ -92,11 +100,13 @@ BlockPlan plan_block(int B, int T, int S, int grid_w, int C, int H, int d, int n
   const bool sliced = n_t > 1 || n_s > 1;
   int64_t rows;
   if (sliced) {
-    p.xb = take(N * C * e);
-    p.hb = take(N * C * e);
     rows = std::max<int64_t>((int64_t)B * (T / n_t) * S, (int64_t)B * (S / n_s) * T);
-    p.xs = take(rows * C * e);
-    p.xs2 = take(rows * C * e);   // slice buffers are double-buffered (two-stream pipeline)
+    if (explicit_copies) p.xb = take(N * C * e);
+    p.hb = take(N * C * e);
+    if (explicit_copies) {
+      p.xs = take(rows * C * e);
+      p.xs2 = take(rows * C * e);   // slice buffers are double-buffered (two-stream pipeline)
+    }
   } else {
     p.xs = take(N * C * e);   // [B,S,T,C] input of the temporal layer (the spatial output, relayout fused)
     rows = N;
@@ -105,11 +115,32 @@ BlockPlan plan_block(int B, int T, int S, int grid_w, int C, int H, int d, int n
   p.k = take(rows * hd * e);
   p.v = take(rows * hd * e);
   p.o = take(rows * hd * e);
-  p.ys = sliced ? take(rows * C * e) : 0;
-  p.ys2 = sliced ? take(rows * C * e) : 0;
+  p.ys = sliced && explicit_copies ? take(rows * C * e) : 0;
+  p.ys2 = sliced && explicit_copies ? take(rows * C * e) : 0;
   p.total = off;
   return p;
 }
+
+}  // namespace
+
+// Scale of q and of the attention inside a layer.  bf16: the projection stores
+// q times (1/sqrt(d)) * log2(e), rounded to bf16 once there, and the attention
+// runs with scale ln 2, so its exponent base-2 argument is the score itself
+// (softmax(q.k/sqrt(d)) unchanged).  fp32: plain q and scale 1/sqrt(d).
+extern "C" st_status st_layer_scales(int d, int dtype, float *q_scale, float *attn_scale) {
+  if (d < 1 || !dtype_ok(dtype) || !q_scale || !attn_scale) return ST_EINVAL;
+  const double s = 1.0 / sqrt((double)d);
+  if (dtype == ST_BF16) {
+    *q_scale = (float)(s * 1.4426950408889634);
+    *attn_scale = (float)0.69314718055994531;
+  } else {
+    *q_scale = 1.0f;
+    *attn_scale = (float)s;
+  }
+  return ST_OK;
+}
+
+namespace {
 
 // One layer: projection + norm/RoPE, attention, output projection.  The
 // projection may read its rows through xmap and the output projection store
@@ -118,9 +149,11 @@ st_status run_layer(const void *x, int64_t outer, int L, int nv, int C, int H, i
                     float eps, const RopeArgs &rope, int dt, void *q, void *k, void *v, void *o, void *y,
                     bool temporal, hipStream_t s, RowMap ymap = {}, RowMap xmap = {}) {
   const int64_t rows = outer * L;
-  st_status r = do_qkv(x, rows, C, w->w_qkv, w->g_q, w->g_k, eps, rope, H, d, dt, q, k, v, s, xmap);
+  float q_scale, attn_scale;
+  st_layer_scales(d, dt, &q_scale, &attn_scale);
+  st_status r = do_qkv(x, rows, C, w->w_qkv, w->g_q, w->g_k, eps, q_scale, rope, H, d, dt, q, k, v, s, xmap);
   if (r != ST_OK) return r;
-  r = do_attn(q, k, v, outer, L, nv, H, d, (float)(1.0 / sqrt((double)d)), dt, o, temporal, s);
+  r = do_attn(q, k, v, outer, L, nv, H, d, attn_scale, dt, o, temporal, s);
   if (r != ST_OK) return r;
   return do_linear(o, rows, H * d, w->w_o, C, dt, y, s, ymap);
 }
@@ -182,10 +215,10 @@ st_status slice_phase(int n, void *const xs[2], void *const ys[2], hipStream_t m
   return ST_OK;
 }
 
-st_status block_sliced(const void *x, int B, int T, int t_valid, int S, int grid_w, int C, int H, int d, int n_t,
-                       int n_s, const st_layer_weights *spatial, const st_layer_weights *temporal, float eps,
-                       float rope_base, int dtype, void *y, void *ws, size_t ws_bytes, hipStream_t s,
-                       hipStream_t side) {
+// Validation of st_block_sliced's arguments other than the workspace (host only).
+st_status check_block(const void *x, int B, int T, int t_valid, int S, int grid_w, int C, int H, int d, int n_t,
+                      int n_s, const st_layer_weights *spatial, const st_layer_weights *temporal, float eps,
+                      float rope_base, int dtype, void *y) {
   if (!dtype_ok(dtype)) return ST_EINVAL;
   if (!x || !y || !spatial || !temporal) return ST_EINVAL;
   for (const st_layer_weights *w : {spatial, temporal})
@@ -202,7 +235,19 @@ st_status block_sliced(const void *x, int B, int T, int t_valid, int S, int grid
     for (const void *p : {w->w_qkv, w->w_o, (const void *)w->g_q, (const void *)w->g_k})
       if (!aligned16(p)) return ST_EALIGN;
   if (!aligned16(x) || !aligned16(y)) return ST_EALIGN;
-  const BlockPlan P = plan_block(B, T, S, grid_w, C, H, d, n_t, n_s, dtype);
+  const int64_t bytes = (int64_t)B * T * S * C * (int64_t)esize(dtype);
+  if (overlap(rng(x, bytes), rng(y, bytes))) return ST_EINVAL;
+  return ST_OK;
+}
+
+st_status block_sliced(const void *x, int B, int T, int t_valid, int S, int grid_w, int C, int H, int d, int n_t,
+                       int n_s, const st_layer_weights *spatial, const st_layer_weights *temporal, float eps,
+                       float rope_base, int dtype, void *y, void *ws, size_t ws_bytes, hipStream_t s,
+                       hipStream_t side) {
+  const st_status c = check_block(x, B, T, t_valid, S, grid_w, C, H, d, n_t, n_s, spatial, temporal, eps, rope_base,
+                                  dtype, y);
+  if (c != ST_OK) return c;
+  const BlockPlan P = plan_block(B, T, S, grid_w, C, H, d, n_t, n_s, dtype, side != s || dtype != ST_BF16);
   if (!ws || ws_bytes < P.total) return ST_EWORKSPACE;
   if (!aligned16(ws)) return ST_EALIGN;
   const size_t e = esize(dtype);
@@ -389,17 +434,18 @@ st_status st_rope_table(int d, int kind, float base, int n_pos, float *table, vo
 }
 
 st_status st_qkv_norm_rope(const void *x, int64_t rows, int c_in, const void *w_qkv, const float *g_q,
-                           const float *g_k, float eps, int rope_kind, const float *rope_table, int rope_npos,
-                           int64_t pos_period, int64_t pos_offset, int grid_w, int H, int d, int dtype, void *q,
-                           void *k, void *v, void *stream) {
+                           const float *g_k, float eps, float q_scale, int rope_kind, const float *rope_table,
+                           int rope_npos, const int32_t *pos, int64_t pos_period, int64_t pos_offset, int grid_w, int H,
+                           int d, int dtype, void *q, void *k, void *v, void *stream) {
   if (!dtype_ok(dtype)) return ST_EINVAL;
   if (!x || !w_qkv || !g_q || !g_k || !q || !k || !v) return ST_EINVAL;
   if (rows < 0 || c_in < 1 || H < 1 || !(eps >= 0.f) || !isfinite(eps)) return ST_EINVAL;
+  if (!(q_scale > 0.f) || !isfinite(q_scale)) return ST_EINVAL;
   if (rope_kind != ST_ROPE_NONE && rope_kind != ST_ROPE_1D && rope_kind != ST_ROPE_2D) return ST_EINVAL;
   if (d < 2 || d % 2 || (rope_kind == ST_ROPE_2D && d % 4)) return ST_EINVAL;
   if (!head_dim_ok(d, dtype, rope_kind)) return ST_EUNSUPPORTED;
   if (dtype == ST_BF16 && c_in % 64) return ST_EUNSUPPORTED;
-  const st_status rs = check_rope(rope_kind, rope_table, rope_npos, pos_period, pos_offset, grid_w, d, rows);
+  const st_status rs = check_rope(rope_kind, rope_table, rope_npos, pos, pos_period, pos_offset, grid_w, d, rows);
   if (rs != ST_OK) return rs;
   if ((int64_t)H * d * 3 >= (1 << 30) || rows >= (1ll << 40)) return ST_EUNSUPPORTED;
   for (const void *p : {x, w_qkv, (const void *)g_q, (const void *)g_k, (const void *)q, (const void *)k,
@@ -411,8 +457,12 @@ st_status st_qkv_norm_rope(const void *x, int64_t rows, int c_in, const void *w_
   for (Range out : {rq, rk, rv})
     if (overlap(out, rx) || overlap(out, rw)) return ST_EINVAL;
   if (overlap(rq, rk) || overlap(rq, rv) || overlap(rk, rv)) return ST_EINVAL;
-  RopeArgs ra{rope_kind, rope_npos, rope_table, pos_period, pos_offset, grid_w};
-  return do_qkv(x, rows, c_in, w_qkv, g_q, g_k, eps, ra, H, d, dtype, q, k, v, (hipStream_t)stream);
+  const int32_t *p = rope_kind == ST_ROPE_NONE ? nullptr : pos;
+  if (p)
+    for (Range out : {rq, rk, rv})
+      if (overlap(out, rng(p, rows * 8))) return ST_EINVAL;
+  RopeArgs ra{rope_kind, rope_npos, rope_table, pos_period, pos_offset, grid_w, p};
+  return do_qkv(x, rows, c_in, w_qkv, g_q, g_k, eps, q_scale, ra, H, d, dtype, q, k, v, (hipStream_t)stream);
 }
 
 st_status st_out_proj(const void *a, int64_t rows, int k_in, const void *w, int n_out, int dtype, void *y,
@@ -585,7 +635,15 @@ size_t st_block_sliced_workspace(int B, int T, int S, int grid_w, int C, int H, 
   if (B < 1 || T < 1 || S < 1 || grid_w < 1 || C < 1 || H < 1 || d < 4 || n_t < 1 || n_s < 1 || !dtype_ok(dtype))
     return 0;
   if (T % n_t || S % n_s || S % grid_w) return 0;
-  return plan_block(B, T, S, grid_w, C, H, d, n_t, n_s, dtype).total;
+  return plan_block(B, T, S, grid_w, C, H, d, n_t, n_s, dtype, dtype != ST_BF16).total;
+}
+
+size_t st_block_sliced_2s_workspace(int B, int T, int S, int grid_w, int C, int H, int d, int n_t, int n_s,
+                                    int dtype) {
+  if (B < 1 || T < 1 || S < 1 || grid_w < 1 || C < 1 || H < 1 || d < 4 || n_t < 1 || n_s < 1 || !dtype_ok(dtype))
+    return 0;
+  if (T % n_t || S % n_s || S % grid_w) return 0;
+  return plan_block(B, T, S, grid_w, C, H, d, n_t, n_s, dtype, true).total;
 }
 
 st_status st_block_sliced(const void *x, int B, int T, int t_valid, int S, int grid_w, int C, int H, int d, int n_t,

@@ -57,6 +57,7 @@ struct RopeArgs {
   const float *table;   // [npos][pairs][2]
   int64_t period, offset;
   int grid_w;
+  const int32_t *pos = nullptr;   // [rows][2] positions ((t, 0) or (h, w)); null: periodic rule
 };
 
 // Row map of a linear layer's input or output rows: row r, read as the
@@ -84,13 +85,14 @@ inline RowMap row_swap(int64_t n1, int64_t n2) {
   return m;
 }
 
+// q is stored multiplied by q_scale (its RMSNorm gain times q_scale).
 st_status launch_qkv_bf16(const void *x, int64_t rows, int c_in, const void *w, const float *g_q,
-                          const float *g_k, float eps, const RopeArgs &rope, int H, int d, void *q,
+                          const float *g_k, float eps, float q_scale, const RopeArgs &rope, int H, int d, void *q,
                           void *k, void *v, hipStream_t s, RowMap xmap = {});
 st_status launch_linear_bf16(const void *a, int64_t rows, int k_in, const void *w, int n_out, void *y,
                              hipStream_t s, RowMap ymap = {});
 st_status launch_qkv_f32(const float *x, int64_t rows, int c_in, const float *w, const float *g_q,
-                         const float *g_k, float eps, const RopeArgs &rope, int H, int d, float *q,
+                         const float *g_k, float eps, float q_scale, const RopeArgs &rope, int H, int d, float *q,
                          float *k, float *v, hipStream_t s);
 st_status launch_linear_f32(const float *a, int64_t rows, int k_in, const float *w, int n_out, float *y,
                             hipStream_t s, RowMap ymap = {});

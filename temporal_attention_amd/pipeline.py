@@ -14,10 +14,11 @@ kernel: torch provides the device buffers, every step is one libst.so call.
 With fused=False the two relayouts are separate st_relayout passes
 (proj_* = st_out_proj into h, then relayout_fwd / relayout_bwd); the results
 are bit-identical.
+
+As in st_block_sliced, q is stored scaled by `q_scale` and the attention runs
+with `scale` (st_layer_scales: in bf16, (1/sqrt(d)) * log2(e) and ln 2).
 """
 from __future__ import annotations
-
-import math
 
 import torch
 
@@ -42,7 +43,7 @@ class LayerPair:
         self.rope1 = torch.empty(L.st_rope_table_floats(d, L.ST_ROPE_1D, T), dtype=torch.float32, device=device)
         L.st_rope_table(d, L.ST_ROPE_2D, rope_base, self.npos2, self.rope2)
         L.st_rope_table(d, L.ST_ROPE_1D, rope_base, T, self.rope1)
-        self.scale = 1.0 / math.sqrt(d)
+        self.q_scale, self.scale = L.st_layer_scales(d, dtype)
         self.hd = hd
         self.x = None
         self.ws = self.wt = None
@@ -61,28 +62,28 @@ class LayerPair:
         if fused:
             return [
                 ("qkv_spatial", lambda: L.st_qkv_norm_rope(
-                    x, N, C, ws["w_qkv"], ws["g_q"], ws["g_k"], self.eps, L.ST_ROPE_2D, self.rope2, self.npos2, S, 0,
-                    self.grid_w, H, d, dt, self.q, self.k, self.v)),
+                    x, N, C, ws["w_qkv"], ws["g_q"], ws["g_k"], self.eps, self.q_scale, L.ST_ROPE_2D, self.rope2,
+                    self.npos2, None, S, 0, self.grid_w, H, d, dt, self.q, self.k, self.v)),
                 ("attn_spatial", lambda: L.st_attn_spatial(self.q, self.k, self.v, B, T, S, H, d, self.scale, dt,
                                                            self.o)),
                 ("proj_spatial", lambda: L.st_out_proj_relayout(self.o, N, self.hd, ws["w_o"], C, dt, T, S, self.hs)),
                 ("qkv_temporal", lambda: L.st_qkv_norm_rope(
-                    self.hs, N, C, wt["w_qkv"], wt["g_q"], wt["g_k"], self.eps, L.ST_ROPE_1D, self.rope1, T, T, 0, 0,
-                    H, d, dt, self.q, self.k, self.v)),
+                    self.hs, N, C, wt["w_qkv"], wt["g_q"], wt["g_k"], self.eps, self.q_scale, L.ST_ROPE_1D, self.rope1,
+                    T, None, T, 0, 0, H, d, dt, self.q, self.k, self.v)),
                 ("attn_temporal", lambda: L.st_attn_temporal(self.q, self.k, self.v, B, S, T, self.t_valid, H, d,
                                                              self.scale, dt, self.o)),
                 ("proj_temporal", lambda: L.st_out_proj_relayout(self.o, N, self.hd, wt["w_o"], C, dt, S, T, self.y)),
             ]
         return [
             ("qkv_spatial", lambda: L.st_qkv_norm_rope(
-                x, N, C, ws["w_qkv"], ws["g_q"], ws["g_k"], self.eps, L.ST_ROPE_2D, self.rope2, self.npos2, S, 0,
-                self.grid_w, H, d, dt, self.q, self.k, self.v)),
+                x, N, C, ws["w_qkv"], ws["g_q"], ws["g_k"], self.eps, self.q_scale, L.ST_ROPE_2D, self.rope2,
+                self.npos2, None, S, 0, self.grid_w, H, d, dt, self.q, self.k, self.v)),
             ("attn_spatial", lambda: L.st_attn_spatial(self.q, self.k, self.v, B, T, S, H, d, self.scale, dt, self.o)),
             ("proj_spatial", lambda: L.st_out_proj(self.o, N, self.hd, ws["w_o"], C, dt, self.h)),
             ("relayout_fwd", lambda: L.st_relayout(self.h, fwd[1], self.hs, fwd[2], fwd[0], 4, eb)),
             ("qkv_temporal", lambda: L.st_qkv_norm_rope(
-                self.hs, N, C, wt["w_qkv"], wt["g_q"], wt["g_k"], self.eps, L.ST_ROPE_1D, self.rope1, T, T, 0, 0, H, d,
-                dt, self.q, self.k, self.v)),
+                self.hs, N, C, wt["w_qkv"], wt["g_q"], wt["g_k"], self.eps, self.q_scale, L.ST_ROPE_1D, self.rope1, T,
+                None, T, 0, 0, H, d, dt, self.q, self.k, self.v)),
             ("attn_temporal", lambda: L.st_attn_temporal(self.q, self.k, self.v, B, S, T, self.t_valid, H, d,
                                                          self.scale, dt, self.o)),
             ("proj_temporal", lambda: L.st_out_proj(self.o, N, self.hd, wt["w_o"], C, dt, self.h)),

@@ -49,9 +49,25 @@ def errors(got, ref):
     return max_abs, rel
 
 
+def assert_close_stored(got, ref, what=""):
+    """bf16 tensors that are stored values (q, k, v), not attention outputs: rel L2 1e-2, and
+    max abs error 2e-2 or one bf16 ulp at the largest magnitude (2^-7 max|ref|), whichever is
+    larger -- rounding a value of magnitude |x| to bf16 alone moves it by up to 2^-8 |x|."""
+    max_abs, rel = errors(got, ref)
+    lim_a = max(BF16_MAX_ABS, 2.0 ** -7 * float(np.max(np.abs(ref))) if np.size(ref) else 0.0)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    assert max_abs <= lim_a and rel <= BF16_REL_L2, f"{what}: max_abs={max_abs:.3e} (bar {lim_a:.3e}) rel_l2={rel:.3e}"
+    return max_abs, rel
+
+
 def assert_close(got, ref, bf16=True, what=""):
     max_abs, rel = errors(got, ref)
     lim_a, lim_r = (BF16_MAX_ABS, BF16_REL_L2) if bf16 else (F32_MAX_ABS, F32_REL_L2)
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     assert max_abs <= lim_a and rel <= lim_r, f"{what}: max_abs={max_abs:.3e} rel_l2={rel:.3e}"
     return max_abs, rel
+
+
+def bf16_round(a) -> np.ndarray:
+    """float64 values rounded to bf16 storage (through fp32, nearest-even), widened back to float64."""
+    return st_synth.to_f64(st_synth.f32_to_bf16_bits(np.asarray(a, np.float64).astype(np.float32)))

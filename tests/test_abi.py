@@ -5,9 +5,11 @@ reject every invalid argument on the host, before any HIP call, with its
 documented status code.  Pointers here are fake aligned addresses: validation
 never dereferences them, and every case below fails validation.
 """
+import math
 import os
 import re
 
+import numpy as np
 import pytest
 
 import temporal_attention_amd as st
@@ -57,9 +59,9 @@ def test_rope_table_validation():
 
 
 def qkv_args(**kw):
-    a = dict(x=P, rows=100, c_in=1152, w_qkv=P2, g_q=P3, g_k=P4, eps=1e-6, rope_kind=st.ST_ROPE_2D, rope_table=P5,
-             rope_npos=120, pos_period=8160, pos_offset=0, grid_w=120, H=16, d=72, dtype=st.ST_BF16, q=BIG,
-             k=2 * BIG, v=3 * BIG)
+    a = dict(x=P, rows=100, c_in=1152, w_qkv=P2, g_q=P3, g_k=P4, eps=1e-6, q_scale=1.0, rope_kind=st.ST_ROPE_2D,
+             rope_table=P5, rope_npos=120, pos=None, pos_period=8160, pos_offset=0, grid_w=120, H=16, d=72,
+             dtype=st.ST_BF16, q=BIG, k=2 * BIG, v=3 * BIG)
     a.update(kw)
     return list(a.values())
 
@@ -85,9 +87,25 @@ def qkv_args(**kw):
     (dict(x=P + 2), st.ST_EALIGN),
     (dict(q=P), st.ST_EINVAL),                        # q aliases x
     (dict(k=BIG + 64), st.ST_EINVAL),                 # k overlaps q
+    (dict(q_scale=0.0), st.ST_EINVAL),
+    (dict(q_scale=float("inf")), st.ST_EINVAL),
+    (dict(pos=P6 + 4), st.ST_EALIGN),                 # positions need 8-byte alignment
+    (dict(pos=BIG + 16), st.ST_EINVAL),               # positions overlap q
+    # with positions the periodic rule is not checked: the call gets past it to the alignment check
+    (dict(pos=P6, pos_period=0, rope_npos=1, x=P + 2), st.ST_EALIGN),
 ])
 def test_qkv_validation(kw, want):
     assert code(st.st_qkv_norm_rope, *qkv_args(**kw)) == want
+
+
+def test_layer_scales():
+    qs, at = st.st_layer_scales(72, st.ST_BF16)
+    assert abs(qs - math.log2(math.e) / math.sqrt(72)) < 1e-7 and abs(at - math.log(2)) < 1e-7
+    # the softmax the layer computes is unchanged: q_scale * attn_scale = 1/sqrt(d)
+    assert abs(qs * at - 1 / math.sqrt(72)) < 1e-7
+    assert st.st_layer_scales(64, st.ST_F32) == (1.0, np.float32(1 / 8.0))
+    with pytest.raises(st.STError):
+        st.st_layer_scales(0, st.ST_BF16)
 
 
 @pytest.mark.parametrize("args,want", [

@@ -5,14 +5,11 @@ and merge the partial results; on one GPU the identity that pins this is
 chunked-then-merged == unchunked.  Inputs are seeded (st_synth), identical
 bytes on both sides.
 
-Tolerances: outputs use the bf16 / fp32 bars of the other kernels.  The bf16
-log-sum-exp is fp32 arithmetic on bf16 operands, and for d = 72 the kernel
-rounds scale*log2(e)*q to bf16 once more before the product (up to 2^-8
-relative per element, round to nearest).  The resulting score error is a
-signed sum of d such terms and grows with the score magnitude, so the bar is
-relative: |lse - lse_ref| <= max(2e-2, 2^-7 * max|lse_ref|) over a call (about
-3-4 standard deviations of that sum at these inputs).  The fp32 path is held to
-1e-4 absolute.
+Tolerances: outputs use the bf16 / fp32 bars of the other kernels (max abs
+2e-2 and rel L2 1e-2 in bf16, 1e-4 in fp32).  The log-sum-exp is a per-query
+scalar of the same attention, held to the same max-abs figures: 2e-2 for the
+bf16 path (fp32 arithmetic on the bf16 operands, which the oracle sees too) and
+1e-4 for fp32.
 """
 import math
 
@@ -36,9 +33,7 @@ LSE_BF16, LSE_F32 = 2e-2, 1e-4
 
 
 def lse_tol(ref, dt):
-    if dt != BF:
-        return LSE_F32
-    return max(LSE_BF16, 2.0 ** -7 * float(np.max(np.abs(ref))) if ref.size else 0.0)
+    return LSE_BF16 if dt == BF else LSE_F32
 
 
 def sync():
@@ -67,6 +62,7 @@ CHUNK_CASES = [
     # outer, Lq, Lk, kv_valid, H, d, q_std, dtype
     (3, 300, 500, 500, 2, 72, 1.0, BF),     # fewer queries than keys
     (2, 257, 100, 77, 3, 72, 3.0, BF),      # masked tail, peaked softmax (many rescales)
+    (1, 300, 1000, 1000, 2, 72, 5.0, BF),   # q std 5: scores of std 5, up to ~20
     (1, 64, 1, 1, 2, 72, 1.0, BF),          # one key
     (2, 100, 130, 130, 2, 128, 1.0, BF),
     (2, 70, 200, 150, 2, 64, 2.0, BF),
