@@ -141,7 +141,8 @@ def time_slicing(x, wsd, wtd, B, T, S, gw, C, H, d, stream, reps):
     def run(nt, ns, two):
         TT = -(-T // nt) * nt
         xx = xv if TT == T else torch.cat([xv, torch.zeros_like(xv[:, :TT - T])], dim=1)
-        nb = st.st_block_sliced_workspace(B, TT, S, gw, C, H, d, nt, ns, st.ST_BF16)
+        query = st.st_block_sliced_2s_workspace if two else st.st_block_sliced_workspace
+        nb = query(B, TT, S, gw, C, H, d, nt, ns, st.ST_BF16)
         ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
         y = torch.empty((B, TT, S, C), dtype=torch.bfloat16, device="cuda")
         if two:

@@ -325,6 +325,10 @@ typedef struct {
  *   spatial, temporal   host pointers to the two layers' weights
  *   y         out  [B, T, S, C]
  *   ws             device workspace of at least st_block_sliced_workspace() bytes
+ *                  (bf16: the blocked intermediate [B, T, S, C] when sliced, or the
+ *                  [B, S, T, C] temporal-layer input when not, plus q, k, v and the
+ *                  attention output for the largest slice; fp32 adds the explicit
+ *                  copies' slice buffers)
  * Each output element is computed by the same arithmetic in the same order
  * whatever n_t and n_s are, so sliced and unsliced results are bit-identical.
  */
@@ -343,7 +347,9 @@ size_t st_block_sliced_workspace(int B, int T, int S, int grid_w, int C, int H, 
  * run on `stream`; the slice gathers, scatters and the two blocked rearranges
  * run on `side_stream`, so slice i's gather overlaps slice i-1's computation
  * and its scatter overlaps slice i+1's.  Slice buffers are double-buffered in
- * the same workspace (st_block_sliced_workspace covers both variants).
+ * the workspace, whose size st_block_sliced_2s_workspace() returns (larger than
+ * st_block_sliced's in bf16: the copies need the blocked input and output and
+ * two sets of slice buffers).
  *
  *   stream, side_stream  two distinct, non-NULL hipStream_t (ST_EINVAL
  *                        otherwise).  The call orders side_stream after the
@@ -359,6 +365,8 @@ st_status st_block_sliced_2s(const void *x, int B, int T, int t_valid, int S, in
                              const st_layer_weights *temporal, float eps, float rope_base,
                              int dtype, void *y, void *ws, size_t ws_bytes, void *stream,
                              void *side_stream);
+size_t st_block_sliced_2s_workspace(int B, int T, int S, int grid_w, int C, int H, int d,
+                                    int n_t, int n_s, int dtype);
 
 #ifdef __cplusplus
 }

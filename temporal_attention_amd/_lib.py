@@ -25,6 +25,7 @@ EXPORTS = (
     "st_status_str", "st_rope_table_floats", "st_rope_table", "st_qkv_norm_rope", "st_layer_scales", "st_out_proj",
     "st_out_proj_relayout", "st_attn_spatial", "st_attn_temporal", "st_attn_chunk", "st_attn_chunk_acc",
     "st_attn_merge", "st_relayout", "st_block_sliced", "st_block_sliced_2s", "st_block_sliced_workspace",
+    "st_block_sliced_2s_workspace",
     "st_v_change",
 )
 
@@ -72,6 +73,7 @@ _SIGS = {
     "st_block_sliced": (_i, [_p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, C.POINTER(st_layer_weights),
                              C.POINTER(st_layer_weights), _f, _f, _i, _p, _p, _sz, _p]),
     "st_block_sliced_workspace": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i, _i, _i]),
+    "st_block_sliced_2s_workspace": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i, _i, _i]),
     "st_block_sliced_2s": (_i, [_p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, C.POINTER(st_layer_weights),
                                 C.POINTER(st_layer_weights), _f, _f, _i, _p, _p, _sz, _p, _p]),
 }
@@ -190,6 +192,10 @@ def layer_weights(w_qkv, w_o, g_q, g_k) -> st_layer_weights:
 
 def st_block_sliced_workspace(B, T, S, grid_w, C_, H, d, n_t, n_s, dtype) -> int:
     return lib.st_block_sliced_workspace(B, T, S, grid_w, C_, H, d, n_t, n_s, dtype)
+
+
+def st_block_sliced_2s_workspace(B, T, S, grid_w, C_, H, d, n_t, n_s, dtype) -> int:
+    return lib.st_block_sliced_2s_workspace(B, T, S, grid_w, C_, H, d, n_t, n_s, dtype)
 
 
 def st_block_sliced(x, B, T, t_valid, S, grid_w, C_, H, d, n_t, n_s, spatial, temporal, eps, rope_base, dtype, y,

@@ -249,7 +249,13 @@ def test_relayout_validation():
 
 def test_block_workspace_and_validation():
     ws = st.st_block_sliced_workspace(1, 52, 8160, 120, 1152, 16, 72, 4, 4, st.ST_BF16)
-    assert ws > 2 * 52 * 8160 * 1152 * 2
+    N, slice_rows = 52 * 8160, max(13 * 8160, 2040 * 52)
+    # one stream, bf16: the blocked intermediate plus q, k, v, o of the largest slice (and two small tables)
+    assert N * 1152 * 2 + 4 * slice_rows * 1152 * 2 <= ws < N * 1152 * 2 + 4 * slice_rows * 1152 * 2 + (1 << 20)
+    ws2 = st.st_block_sliced_2s_workspace(1, 52, 8160, 120, 1152, 16, 72, 4, 4, st.ST_BF16)
+    assert ws2 >= ws + N * 1152 * 2 + 4 * slice_rows * 1152 * 2      # + blocked input, 2 x 2 slice buffers
+    f32 = (1, 4, 64, 8, 128, 2, 64, 2, 2, st.ST_F32)    # fp32 always copies explicitly
+    assert st.st_block_sliced_workspace(*f32) == st.st_block_sliced_2s_workspace(*f32)
     assert st.st_block_sliced_workspace(1, 51, 8160, 120, 1152, 16, 72, 4, 4, st.ST_BF16) == 0   # T % n_t
     w = st.layer_weights(P, P2, P3, P4)
     bad_w = st.layer_weights(P, None, P3, P4)

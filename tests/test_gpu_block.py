@@ -49,7 +49,8 @@ def host_weights(w):
 def run_block(xd, wd, T, t_valid, S, grid_w, C, H, d, n_t, n_s, dt, two_streams=False, B=1):
     sp = st.layer_weights(wd["s"]["w_qkv"], wd["s"]["w_o"], wd["s"]["g_q"], wd["s"]["g_k"])
     tp = st.layer_weights(wd["t"]["w_qkv"], wd["t"]["w_o"], wd["t"]["g_q"], wd["t"]["g_k"])
-    nbytes = st.st_block_sliced_workspace(B, T, S, grid_w, C, H, d, n_t, n_s, dt)
+    query = st.st_block_sliced_2s_workspace if two_streams else st.st_block_sliced_workspace
+    nbytes = query(B, T, S, grid_w, C, H, d, n_t, n_s, dt)
     ws = t_.empty(nbytes, dtype=t_.uint8, device="cuda")
     y = empty((B, T, S, C), dt == st.ST_BF16)
     if two_streams:   # slice gathers/scatters on a second stream (default priority)
