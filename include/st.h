@@ -368,6 +368,32 @@ st_status st_block_sliced_2s(const void *x, int B, int T, int t_valid, int S, in
 size_t st_block_sliced_2s_workspace(int B, int T, int S, int grid_w, int C, int H, int d,
                                     int n_t, int n_s, int dtype);
 
+/*
+ * st_block_sliced_noalloc -- st_block_sliced for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments without the workspace, which is
+ * taken from a fixed device array inside the library instead.  The call
+ * allocates nothing and frees nothing; the result is bit-identical to
+ * st_block_sliced on the same arguments.
+ *
+ *   Limit: the workspace st_block_sliced_workspace() reports for the arguments
+ *   must be at most st_block_sliced_noalloc_max() bytes (256 MiB), else
+ *   ST_EWORKSPACE before any GPU work.  For example the layer pair of 16 heads
+ *   x 72, C = 1152, fits up to about 23,000 tokens per call (B*T*S).
+ *   The array exists once per GPU the library runs on and stays allocated
+ *   until the process ends.  Every call on one GPU uses that GPU's copy, so
+ *   calls that overlap in time on one GPU (other streams, other host threads)
+ *   race on it: the caller must order them.  Nothing in it needs to start at
+ *   zero; a call overwrites what it reads.
+ * Validation and error codes as st_block_sliced, plus ST_ELAUNCH if the
+ * array's device address cannot be obtained.
+ */
+st_status st_block_sliced_noalloc(const void *x, int B, int T, int t_valid, int S, int grid_w, int C,
+                                  int H, int d, int n_t, int n_s, const st_layer_weights *spatial,
+                                  const st_layer_weights *temporal, float eps, float rope_base,
+                                  int dtype, void *y, void *stream);
+size_t st_block_sliced_noalloc_max(void);
+
 #ifdef __cplusplus
 }
 #endif

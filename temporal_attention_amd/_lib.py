@@ -25,7 +25,7 @@ EXPORTS = (
     "st_status_str", "st_rope_table_floats", "st_rope_table", "st_qkv_norm_rope", "st_layer_scales", "st_out_proj",
     "st_out_proj_relayout", "st_attn_spatial", "st_attn_temporal", "st_attn_chunk", "st_attn_chunk_acc",
     "st_attn_merge", "st_relayout", "st_block_sliced", "st_block_sliced_2s", "st_block_sliced_workspace",
-    "st_block_sliced_2s_workspace",
+    "st_block_sliced_2s_workspace", "st_block_sliced_noalloc", "st_block_sliced_noalloc_max",
     "st_v_change",
 )
 
@@ -74,6 +74,9 @@ _SIGS = {
                              C.POINTER(st_layer_weights), _f, _f, _i, _p, _p, _sz, _p]),
     "st_block_sliced_workspace": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i, _i, _i]),
     "st_block_sliced_2s_workspace": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i, _i, _i]),
+    "st_block_sliced_noalloc": (_i, [_p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, C.POINTER(st_layer_weights),
+                                     C.POINTER(st_layer_weights), _f, _f, _i, _p, _p]),
+    "st_block_sliced_noalloc_max": (_sz, []),
     "st_block_sliced_2s": (_i, [_p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, C.POINTER(st_layer_weights),
                                 C.POINTER(st_layer_weights), _f, _f, _i, _p, _p, _sz, _p, _p]),
 }
@@ -205,6 +208,20 @@ def st_block_sliced(x, B, T, t_valid, S, grid_w, C_, H, d, n_t, n_s, spatial, te
     tp = C.byref(temporal) if temporal is not None else None
     _check("st_block_sliced", lib.st_block_sliced(_ptr(x), B, T, t_valid, S, grid_w, C_, H, d, n_t, n_s, sp, tp, eps,
                                                   rope_base, dtype, _ptr(y), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def st_block_sliced_noalloc(x, B, T, t_valid, S, grid_w, C_, H, d, n_t, n_s, spatial, temporal, eps, rope_base, dtype,
+                            y, stream=None):
+    """As st_block_sliced, with the workspace taken from the library's fixed device array."""
+    sp = C.byref(spatial) if spatial is not None else None
+    tp = C.byref(temporal) if temporal is not None else None
+    _check("st_block_sliced_noalloc", lib.st_block_sliced_noalloc(_ptr(x), B, T, t_valid, S, grid_w, C_, H, d, n_t, n_s,
+                                                                  sp, tp, eps, rope_base, dtype, _ptr(y),
+                                                                  _stream(stream)))
+
+
+def st_block_sliced_noalloc_max() -> int:
+    return lib.st_block_sliced_noalloc_max()
 
 
 def st_block_sliced_2s(x, B, T, t_valid, S, grid_w, C_, H, d, n_t, n_s, spatial, temporal, eps, rope_base, dtype, y,

@@ -5,10 +5,18 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "st_internal.h"
 
 using namespace st;
+
+// Device scratch of st_block_sliced_noalloc: every GPU the library runs on
+// holds one copy of this array until the process ends.  Host code never uses
+// the array's name as an address (on the host it is only a stand-in); it uses
+// the per-device address that hipGetSymbolAddress returns.
+constexpr size_t kScratchBytes = size_t(256) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -651,6 +659,41 @@ st_status st_block_sliced(const void *x, int B, int T, int t_valid, int S, int g
                           float rope_base, int dtype, void *y, void *ws, size_t ws_bytes, void *stream) {
   return block_sliced(x, B, T, t_valid, S, grid_w, C, H, d, n_t, n_s, spatial, temporal, eps, rope_base, dtype, y, ws,
                       ws_bytes, (hipStream_t)stream, (hipStream_t)stream);
+}
+
+// Per-device address of the scratch array, looked up once per device, with
+// that device current, on the first call there.
+static std::mutex scratch_mu;
+static void *scratch_dev[64];
+
+static st_status scratch_for_current_device(void **p) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return ST_ELAUNCH;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_dev[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return ST_ELAUNCH;
+    scratch_dev[dev] = ptr;
+  }
+  *p = scratch_dev[dev];
+  return ST_OK;
+}
+
+size_t st_block_sliced_noalloc_max(void) { return kScratchBytes; }
+
+st_status st_block_sliced_noalloc(const void *x, int B, int T, int t_valid, int S, int grid_w, int C, int H, int d,
+                                  int n_t, int n_s, const st_layer_weights *spatial, const st_layer_weights *temporal,
+                                  float eps, float rope_base, int dtype, void *y, void *stream) {
+  const st_status c = check_block(x, B, T, t_valid, S, grid_w, C, H, d, n_t, n_s, spatial, temporal, eps, rope_base,
+                                  dtype, y);
+  if (c != ST_OK) return c;
+  const size_t need = st_block_sliced_workspace(B, T, S, grid_w, C, H, d, n_t, n_s, dtype);
+  if (need == 0 || need > kScratchBytes) return ST_EWORKSPACE;
+  void *ws = nullptr;
+  const st_status r = scratch_for_current_device(&ws);
+  if (r != ST_OK) return r;
+  return block_sliced(x, B, T, t_valid, S, grid_w, C, H, d, n_t, n_s, spatial, temporal, eps, rope_base, dtype, y, ws,
+                      kScratchBytes, (hipStream_t)stream, (hipStream_t)stream);
 }
 
 st_status st_block_sliced_2s(const void *x, int B, int T, int t_valid, int S, int grid_w, int C, int H, int d, int n_t,

@@ -283,3 +283,15 @@ def test_block_workspace_and_validation():
     assert c(d=80) == st.ST_EUNSUPPORTED
     assert c(y=P5) == st.ST_EINVAL                 # y aliases x
     assert c(x=P5 + 2) == st.ST_EALIGN
+
+
+def test_block_noalloc_rejects_beyond_its_scratch_before_any_gpu_work():
+    assert st.st_block_sliced_noalloc_max() == 256 << 20
+    w = st.layer_weights(P, P2, P3, P4)
+    # the 720p layer pair needs ~1 GB of workspace
+    args = [P5, 1, 24, 24, 3600, 80, 1152, 16, 72, 1, 1, w, w, 1e-6, 10000.0, st.ST_BF16, BIG]
+    assert code(st.st_block_sliced_noalloc, *args) == st.ST_EWORKSPACE
+    args[9:11] = [4, 4]
+    assert code(st.st_block_sliced_noalloc, *args) == st.ST_EWORKSPACE
+    args[2] = 25                                                       # T % n_t
+    assert code(st.st_block_sliced_noalloc, *args) == st.ST_EINVAL
