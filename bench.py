@@ -237,7 +237,7 @@ def time_image_attention(reps, stream):
     g.manual_seed(4096)
     q, k, v = (torch.randn((1, S, H, d), device="cuda", generator=g).to(torch.bfloat16) for _ in range(3))
     o = torch.empty_like(q)
-    run = lambda: st.st_attn_spatial(q, k, v, 1, 1, S, H, d, 1.0 / math.sqrt(d), st.ST_BF16, o)  # noqa: E731
+    run = lambda: st.st_attn_spatial(q, k, v, 1, 1, S, H, d, 1.0 / math.sqrt(d), st.ST_BF16, None, 0, o)  # noqa: E731
     run()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -264,8 +264,8 @@ def time_a2a_local(B, T, S, C, P, reps, stream):
     xs = torch.empty((B, TT, sp, C), dtype=torch.bfloat16, device="cuda")   # contents irrelevant to a copy
     xt = torch.empty((B, tp, S, C), dtype=torch.bfloat16, device="cuda")
     buf = torch.empty((P, B, tp, sp, C), dtype=torch.bfloat16, device="cuda")
-    ops = {"pack_s2t": lambda: a2a.pack_s2t(xs, buf, B, TT, sp, C, P),
-           "unpack_s2t": lambda: a2a.unpack_s2t(buf, xt, B, TT, sp, C, P),
+    ops = {"pack_s2t": lambda: a2a.pack_s2t(xs, buf, B, TT, S, C, P),
+           "unpack_s2t": lambda: a2a.unpack_s2t(buf, xt, B, TT, S, C, P),
            "pack_t2s": lambda: a2a.pack_t2s(xt, buf, B, TT, S, C, P),
            "unpack_t2s": lambda: a2a.unpack_t2s(buf, xs, B, TT, S, C, P)}
     nbytes = 2.0 * xs.numel() * 2

@@ -59,6 +59,11 @@ typedef enum {
 typedef enum { ST_F32 = 0, ST_BF16 = 1 } st_dtype;
 
 typedef enum {
+  ST_A2A_S2T = 0,       /* patch blocks [B, T, S/P, C] -> frame blocks [B, T/P, S, C]  */
+  ST_A2A_T2S = 1        /* frame blocks [B, T/P, S, C] -> patch blocks [B, T, S/P, C]  */
+} st_a2a_dir;
+
+typedef enum {
   ST_ROPE_NONE = 0,     /* no rotation                                         */
   ST_ROPE_1D = 1,       /* one segment over all d channels, position p = t     */
   ST_ROPE_2D = 2        /* axial: channels [0, d/2) by patch row h,
@@ -168,12 +173,23 @@ st_status st_out_proj_relayout(const void *a, int64_t rows, int k_in, const void
  *
  *   q, k, v  in   [B, T, S, H, d]   (the [rows, H, d] output of st_qkv_norm_rope
  *                                     for rows in [B, T, S] order)
- *   out      out  [B, T, S, H, d]
- *   scale         usually 1/sqrt(d); passed by the caller
- * Same d support as st_qkv_norm_rope.  S >= 1.
+ *   scale         usually 1/sqrt(d); passed by the caller.  bf16, d = 72: when
+ *                 scale * log2(e) is a power of two (scale = ln 2 with q stored
+ *                 pre-scaled, see st_layer_scales) the kernel needs no multiply
+ *                 in the exponent; any other scale costs one multiply per score
+ *                 (about 8% at 1080p), same precision
+ *   w_o      in   NULL, or the layer's output projection [c_out, H*d]
+ *   c_out         output channels when w_o is given (multiple of 4)
+ *   out      out  w_o NULL: O [B, T, S, H, d];  else O . w_o^T [B, T, S, c_out]
+ *   ws, ws_bytes  w_o given: device workspace of at least st_attn_workspace(B*T*S, H, d,
+ *                 dtype) bytes, where O is staged (else ignored; may be NULL)
+ * Same d support as st_qkv_norm_rope; bf16 with w_o needs H*d % 64 == 0.  S >= 1.
  */
 st_status st_attn_spatial(const void *q, const void *k, const void *v, int B, int T, int S,
-                          int H, int d, float scale, int dtype, void *out, void *stream);
+                          int H, int d, float scale, int dtype, const void *w_o, int c_out,
+                          void *out, void *ws, size_t ws_bytes, void *stream);
+/* Bytes of workspace an attention call with w_o needs for `rows` query rows (0 if invalid). */
+size_t st_attn_workspace(int64_t rows, int H, int d, int dtype);
 
 /*
  * st_attn_temporal -- temporal attention: for every (b, s, h),
@@ -184,12 +200,13 @@ st_status st_attn_spatial(const void *q, const void *k, const void *v, int B, in
  * ScaleFusion review, "Technical architecture" (the temporal layer attends over T).
  *
  *   q, k, v  in   [B, S, T, H, d]
- *   out      out  [B, S, T, H, d]
  *   1 <= t_valid <= T.
+ *   scale, w_o, c_out, ws, ws_bytes   as st_attn_spatial (rows = B*S*T)
+ *   out      out  w_o NULL: O [B, S, T, H, d];  else O . w_o^T [B, S, T, c_out]
  */
 st_status st_attn_temporal(const void *q, const void *k, const void *v, int B, int S, int T,
-                           int t_valid, int H, int d, float scale, int dtype, void *out,
-                           void *stream);
+                           int t_valid, int H, int d, float scale, int dtype, const void *w_o,
+                           int c_out, void *out, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * st_attn_chunk -- attention of queries over ONE chunk of keys/values, with the
@@ -294,6 +311,37 @@ st_status st_v_change(const void *v_new, void *v_cache, int64_t rows, int H, int
 st_status st_relayout(const void *src, const int64_t *src_strides, void *dst,
                       const int64_t *dst_strides, const int64_t *dims, int ndim,
                       int elem_bytes, void *stream);
+
+/*
+ * st_a2a_pack / st_a2a_unpack -- one rank's local pack before, and unpack after,
+ * the P-way all-to-all between the two shardings of the layer pair (ScaleFusion
+ * review, "Technical architecture": the layer table gives each rank [B, T, S/P, C]
+ * for the temporal layer and [B, T/P, S, C] for the spatial layer, and an
+ * all-to-all converts between them; "Core innovations", algorithm pseudocode:
+ * the exchange sits between the layers).  A collective moves one contiguous
+ * chunk per peer, so the exchange is pack -> all-to-all -> unpack.  Chunk layout
+ * on the wire, both directions: [P, B, T/P, S/P, C], chunk q contiguous.
+ *
+ *   dir = ST_A2A_S2T (before the spatial layer):
+ *     pack    x    [B, T, S/P, C]   this rank's patch block  -> send [P, B, T/P, S/P, C],
+ *                                   chunk q = frames q*T/P .. (q+1)*T/P - 1
+ *     unpack  recv [P, B, T/P, S/P, C], chunk r from rank r  -> y [B, T/P, S, C],
+ *                                   rank r's patches at r*S/P ..
+ *   dir = ST_A2A_T2S (before the temporal layer):
+ *     pack    x    [B, T/P, S, C]   this rank's frame block  -> send [P, B, T/P, S/P, C],
+ *                                   chunk q = patches q*S/P .. (q+1)*S/P - 1
+ *     unpack  recv [P, B, T/P, S/P, C], chunk r from rank r  -> y [B, T, S/P, C],
+ *                                   rank r's frames at r*T/P ..
+ *   T, S        the GLOBAL frame and patch counts; T % P == 0 and S % P == 0
+ *               (pad T with masked frames first, as for the slicing schedule)
+ *   elem_bytes  1, 2, 4 or 8; pointers aligned to it
+ * Both buffers hold B*T*S*C/P elements and must not overlap (ST_EINVAL).
+ * Bit-exact copies (one st_relayout pass each).  P = 1 is a plain copy.
+ */
+st_status st_a2a_pack(const void *x, void *send, int dir, int B, int T, int S, int C, int P,
+                      int elem_bytes, void *stream);
+st_status st_a2a_unpack(const void *recv, void *y, int dir, int B, int T, int S, int C, int P,
+                        int elem_bytes, void *stream);
 
 /* Weights of one layer (all device pointers). */
 typedef struct {

@@ -19,13 +19,16 @@ LIB_PATH = os.path.join(_PKG, "libst.so")
 ST_OK, ST_EINVAL, ST_EUNSUPPORTED, ST_EALIGN, ST_EWORKSPACE, ST_ELAUNCH = range(6)
 ST_F32, ST_BF16 = 0, 1
 ST_ROPE_NONE, ST_ROPE_1D, ST_ROPE_2D = 0, 1, 2
+ST_A2A_S2T, ST_A2A_T2S = 0, 1
 
 # Every entry point declared in include/st.h.
 EXPORTS = (
     "st_status_str", "st_rope_table_floats", "st_rope_table", "st_qkv_norm_rope", "st_layer_scales", "st_out_proj",
-    "st_out_proj_relayout", "st_attn_spatial", "st_attn_temporal", "st_attn_chunk", "st_attn_chunk_acc",
+    "st_out_proj_relayout", "st_attn_spatial", "st_attn_temporal", "st_attn_workspace", "st_attn_chunk",
+    "st_attn_chunk_acc",
     "st_attn_merge", "st_relayout", "st_block_sliced", "st_block_sliced_2s", "st_block_sliced_workspace",
-    "st_block_sliced_2s_workspace", "st_block_sliced_noalloc", "st_block_sliced_noalloc_max",
+    "st_block_sliced_2s_workspace", "st_block_sliced_noalloc", "st_block_sliced_noalloc_max", "st_a2a_pack",
+    "st_a2a_unpack",
     "st_v_change",
 )
 
@@ -63,8 +66,9 @@ _SIGS = {
     "st_layer_scales": (_i, [_i, _i, C.POINTER(C.c_float), C.POINTER(C.c_float)]),
     "st_out_proj": (_i, [_p, _i64, _i, _p, _i, _i, _p, _p]),
     "st_out_proj_relayout": (_i, [_p, _i64, _i, _p, _i, _i, _i64, _i64, _p, _p]),
-    "st_attn_spatial": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p, _p]),
-    "st_attn_temporal": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p, _p]),
+    "st_attn_spatial": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p, _i, _p, _p, _sz, _p]),
+    "st_attn_temporal": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p, _i, _p, _p, _sz, _p]),
+    "st_attn_workspace": (_sz, [_i64, _i, _i, _i]),
     "st_attn_chunk": (_i, [_p, _p, _p, _i64, _i, _i, _i, _i, _i, _f, _i, _p, _p, _p]),
     "st_attn_chunk_acc": (_i, [_p, _p, _p, _i64, _i, _i, _i, _i, _i, _f, _i, _p, _p, _p]),
     "st_attn_merge": (_i, [_p, _p, _p, _p, _i64, _i, _i, _i, _i, _p, _p, _p]),
@@ -77,6 +81,8 @@ _SIGS = {
     "st_block_sliced_noalloc": (_i, [_p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, C.POINTER(st_layer_weights),
                                      C.POINTER(st_layer_weights), _f, _f, _i, _p, _p]),
     "st_block_sliced_noalloc_max": (_sz, []),
+    "st_a2a_pack": (_i, [_p, _p, _i, _i, _i, _i, _i, _i, _i, _p]),
+    "st_a2a_unpack": (_i, [_p, _p, _i, _i, _i, _i, _i, _i, _i, _p]),
     "st_block_sliced_2s": (_i, [_p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, C.POINTER(st_layer_weights),
                                 C.POINTER(st_layer_weights), _f, _f, _i, _p, _p, _sz, _p, _p]),
 }
@@ -148,14 +154,20 @@ def st_out_proj_relayout(a, rows, k_in, w, n_out, dtype, n1, n2, y, stream=None)
                                                             _ptr(y), _stream(stream)))
 
 
-def st_attn_spatial(q, k, v, B, T, S, H, d, scale, dtype, out, stream=None):
-    _check("st_attn_spatial", lib.st_attn_spatial(_ptr(q), _ptr(k), _ptr(v), B, T, S, H, d, scale, dtype, _ptr(out),
-                                                  _stream(stream)))
+def st_attn_spatial(q, k, v, B, T, S, H, d, scale, dtype, w_o, c_out, out, ws=None, ws_bytes=0, stream=None):
+    _check("st_attn_spatial", lib.st_attn_spatial(_ptr(q), _ptr(k), _ptr(v), B, T, S, H, d, scale, dtype, _ptr(w_o),
+                                                  c_out, _ptr(out), _ptr(ws), ws_bytes, _stream(stream)))
 
 
-def st_attn_temporal(q, k, v, B, S, T, t_valid, H, d, scale, dtype, out, stream=None):
+def st_attn_temporal(q, k, v, B, S, T, t_valid, H, d, scale, dtype, w_o, c_out, out, ws=None, ws_bytes=0,
+                     stream=None):
     _check("st_attn_temporal", lib.st_attn_temporal(_ptr(q), _ptr(k), _ptr(v), B, S, T, t_valid, H, d, scale, dtype,
-                                                    _ptr(out), _stream(stream)))
+                                                    _ptr(w_o), c_out, _ptr(out), _ptr(ws), ws_bytes,
+                                                    _stream(stream)))
+
+
+def st_attn_workspace(rows, H, d, dtype) -> int:
+    return lib.st_attn_workspace(rows, H, d, dtype)
 
 
 def st_attn_chunk(q, k, v, outer, Lq, Lk, kv_valid, H, d, scale, dtype, out, lse, stream=None):
@@ -187,6 +199,14 @@ def _i64arr(vals):
 def st_relayout(src, src_strides, dst, dst_strides, dims, ndim, elem_bytes, stream=None):
     _check("st_relayout", lib.st_relayout(_ptr(src), _i64arr(src_strides), _ptr(dst), _i64arr(dst_strides),
                                           _i64arr(dims), ndim, elem_bytes, _stream(stream)))
+
+
+def st_a2a_pack(x, send, dir, B, T, S, C_, P, elem_bytes, stream=None):
+    _check("st_a2a_pack", lib.st_a2a_pack(_ptr(x), _ptr(send), dir, B, T, S, C_, P, elem_bytes, _stream(stream)))
+
+
+def st_a2a_unpack(recv, y, dir, B, T, S, C_, P, elem_bytes, stream=None):
+    _check("st_a2a_unpack", lib.st_a2a_unpack(_ptr(recv), _ptr(y), dir, B, T, S, C_, P, elem_bytes, _stream(stream)))
 
 
 def layer_weights(w_qkv, w_o, g_q, g_k) -> st_layer_weights:

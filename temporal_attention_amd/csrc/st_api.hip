@@ -500,32 +500,56 @@ st_status st_out_proj_relayout(const void *a, int64_t rows, int k_in, const void
   return do_linear(a, rows, k_in, w, n_out, dtype, y, (hipStream_t)stream, row_swap(n1, n2));
 }
 
+size_t st_attn_workspace(int64_t rows, int H, int d, int dtype) {
+  if (rows < 0 || H < 1 || d < 1 || !dtype_ok(dtype) || rows >= (1ll << 40)) return 0;
+  return align256((size_t)rows * H * d * esize(dtype));
+}
+
+// w_o != NULL: the attention output is staged in ws and out = O . w_o^T.
 static st_status attn_common(const void *q, const void *k, const void *v, int64_t outer, int L, int nv, int H, int d,
-                             float scale, int dtype, void *out, bool temporal, void *stream) {
+                             float scale, int dtype, const void *w_o, int c_out, void *out, void *ws, size_t ws_bytes,
+                             bool temporal, void *stream) {
   if (!dtype_ok(dtype)) return ST_EINVAL;
   if (!q || !k || !v || !out || H < 1 || d < 2 || d % 2) return ST_EINVAL;
   if (!(scale > 0.f) || !isfinite(scale)) return ST_EINVAL;
+  if (w_o && c_out < 1) return ST_EINVAL;
   if (!head_dim_ok(d, dtype, ST_ROPE_NONE)) return ST_EUNSUPPORTED;
   if (outer >= (1ll << 40) || L >= (1 << 30)) return ST_EUNSUPPORTED;
+  if (w_o && (c_out % 4 || (dtype == ST_BF16 && (H * d) % 64) || (int64_t)H * d * c_out >= (1ll << 31)))
+    return ST_EUNSUPPORTED;
   for (const void *p : {q, k, v, (const void *)out})
     if (!aligned16(p)) return ST_EALIGN;
-  const int64_t bytes = outer * L * H * d * (int64_t)esize(dtype);
-  const Range ro = rng(out, bytes);
-  if (overlap(ro, rng(q, bytes)) || overlap(ro, rng(k, bytes)) || overlap(ro, rng(v, bytes))) return ST_EINVAL;
-  return do_attn(q, k, v, outer, L, nv, H, d, scale, dtype, out, temporal, (hipStream_t)stream);
+  const int64_t rows = outer * L;
+  const int64_t e = (int64_t)esize(dtype), bytes = rows * H * d * e;
+  const Range rq = rng(q, bytes), rk = rng(k, bytes), rv = rng(v, bytes);
+  const Range ro = rng(out, w_o ? rows * c_out * e : bytes);
+  if (overlap(ro, rq) || overlap(ro, rk) || overlap(ro, rv)) return ST_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  if (!w_o) return do_attn(q, k, v, outer, L, nv, H, d, scale, dtype, out, temporal, s);
+  if (!ws || ws_bytes < st_attn_workspace(rows, H, d, dtype)) return ST_EWORKSPACE;
+  if (!aligned16(w_o) || !aligned16(ws)) return ST_EALIGN;
+  const Range rw = rng(w_o, (int64_t)c_out * H * d * e), rs = rng(ws, bytes);
+  if (overlap(ro, rw) || overlap(ro, rs)) return ST_EINVAL;
+  for (const Range &in : {rq, rk, rv, rw})
+    if (overlap(rs, in)) return ST_EINVAL;
+  const st_status r = do_attn(q, k, v, outer, L, nv, H, d, scale, dtype, ws, temporal, s);
+  if (r != ST_OK) return r;
+  return do_linear(ws, rows, H * d, w_o, c_out, dtype, out, s);
 }
 
 st_status st_attn_spatial(const void *q, const void *k, const void *v, int B, int T, int S, int H, int d, float scale,
-                          int dtype, void *out, void *stream) {
+                          int dtype, const void *w_o, int c_out, void *out, void *ws, size_t ws_bytes, void *stream) {
   if (B < 0 || T < 0 || S < 0) return ST_EINVAL;
-  return attn_common(q, k, v, (int64_t)B * T, S, S, H, d, scale, dtype, out, false, stream);
+  return attn_common(q, k, v, (int64_t)B * T, S, S, H, d, scale, dtype, w_o, c_out, out, ws, ws_bytes, false, stream);
 }
 
 st_status st_attn_temporal(const void *q, const void *k, const void *v, int B, int S, int T, int t_valid, int H, int d,
-                           float scale, int dtype, void *out, void *stream) {
+                           float scale, int dtype, const void *w_o, int c_out, void *out, void *ws, size_t ws_bytes,
+                           void *stream) {
   if (B < 0 || S < 0 || T < 0) return ST_EINVAL;
   if (T > 0 && (t_valid < 1 || t_valid > T)) return ST_EINVAL;
-  return attn_common(q, k, v, (int64_t)B * S, T, t_valid, H, d, scale, dtype, out, true, stream);
+  return attn_common(q, k, v, (int64_t)B * S, T, t_valid, H, d, scale, dtype, w_o, c_out, out, ws, ws_bytes, true,
+                     stream);
 }
 
 static st_status chunk_check(const void *q, const void *k, const void *v, int64_t outer, int Lq, int Lk, int kv_valid,

@@ -65,27 +65,28 @@ class LayerPair:
                     x, N, C, ws["w_qkv"], ws["g_q"], ws["g_k"], self.eps, self.q_scale, L.ST_ROPE_2D, self.rope2,
                     self.npos2, None, S, 0, self.grid_w, H, d, dt, self.q, self.k, self.v)),
                 ("attn_spatial", lambda: L.st_attn_spatial(self.q, self.k, self.v, B, T, S, H, d, self.scale, dt,
-                                                           self.o)),
+                                                           None, 0, self.o)),
                 ("proj_spatial", lambda: L.st_out_proj_relayout(self.o, N, self.hd, ws["w_o"], C, dt, T, S, self.hs)),
                 ("qkv_temporal", lambda: L.st_qkv_norm_rope(
                     self.hs, N, C, wt["w_qkv"], wt["g_q"], wt["g_k"], self.eps, self.q_scale, L.ST_ROPE_1D, self.rope1,
                     T, None, T, 0, 0, H, d, dt, self.q, self.k, self.v)),
                 ("attn_temporal", lambda: L.st_attn_temporal(self.q, self.k, self.v, B, S, T, self.t_valid, H, d,
-                                                             self.scale, dt, self.o)),
+                                                             self.scale, dt, None, 0, self.o)),
                 ("proj_temporal", lambda: L.st_out_proj_relayout(self.o, N, self.hd, wt["w_o"], C, dt, S, T, self.y)),
             ]
         return [
             ("qkv_spatial", lambda: L.st_qkv_norm_rope(
                 x, N, C, ws["w_qkv"], ws["g_q"], ws["g_k"], self.eps, self.q_scale, L.ST_ROPE_2D, self.rope2,
                 self.npos2, None, S, 0, self.grid_w, H, d, dt, self.q, self.k, self.v)),
-            ("attn_spatial", lambda: L.st_attn_spatial(self.q, self.k, self.v, B, T, S, H, d, self.scale, dt, self.o)),
+            ("attn_spatial", lambda: L.st_attn_spatial(self.q, self.k, self.v, B, T, S, H, d, self.scale, dt, None, 0,
+                                                       self.o)),
             ("proj_spatial", lambda: L.st_out_proj(self.o, N, self.hd, ws["w_o"], C, dt, self.h)),
             ("relayout_fwd", lambda: L.st_relayout(self.h, fwd[1], self.hs, fwd[2], fwd[0], 4, eb)),
             ("qkv_temporal", lambda: L.st_qkv_norm_rope(
                 self.hs, N, C, wt["w_qkv"], wt["g_q"], wt["g_k"], self.eps, self.q_scale, L.ST_ROPE_1D, self.rope1, T,
                 None, T, 0, 0, H, d, dt, self.q, self.k, self.v)),
             ("attn_temporal", lambda: L.st_attn_temporal(self.q, self.k, self.v, B, S, T, self.t_valid, H, d,
-                                                         self.scale, dt, self.o)),
+                                                         self.scale, dt, None, 0, self.o)),
             ("proj_temporal", lambda: L.st_out_proj(self.o, N, self.hd, wt["w_o"], C, dt, self.h)),
             ("relayout_bwd", lambda: L.st_relayout(self.h, bwd[1], self.y, bwd[2], bwd[0], 4, eb)),
         ]

@@ -137,22 +137,47 @@ def test_out_proj_relayout_validation(args, want):
     assert code(st.st_out_proj_relayout, *args) == want
 
 
-@pytest.mark.parametrize("args,want", [
-    ((None, P2, P3, 1, 51, 8160, 16, 72, 0.1, st.ST_BF16, BIG), st.ST_EINVAL),
-    ((P, P2, P3, 1, 51, 8160, 16, 72, 0.0, st.ST_BF16, BIG), st.ST_EINVAL),       # scale must be > 0
-    ((P, P2, P3, 1, 51, 8160, 16, 72, float("nan"), st.ST_BF16, BIG), st.ST_EINVAL),
-    ((P, P2, P3, -1, 51, 8160, 16, 72, 0.1, st.ST_BF16, BIG), st.ST_EINVAL),
-    ((P, P2, P3, 1, 51, 8160, 16, 80, 0.1, st.ST_BF16, BIG), st.ST_EUNSUPPORTED),
-    ((P, P2, P3, 1, 51, 8160, 16, 72, 0.1, st.ST_BF16, P), st.ST_EINVAL),         # out aliases q
-    ((P, P2, P3, 1, 51, 8160, 16, 72, 0.1, st.ST_BF16, BIG + 8), st.ST_EALIGN),
+def attn_args(**kw):
+    a = dict(q=P, k=P2, v=P3, B=1, T=51, S=8160, H=16, d=72, scale=0.1, dtype=st.ST_BF16, w_o=None, c_out=0,
+             out=BIG, ws=None, ws_bytes=0)
+    a.update(kw)
+    return list(a.values())
+
+
+ROWS = 51 * 8160
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), st.ST_EINVAL),
+    (dict(scale=0.0), st.ST_EINVAL),                   # scale must be > 0
+    (dict(scale=float("nan")), st.ST_EINVAL),
+    (dict(B=-1), st.ST_EINVAL),
+    (dict(d=80), st.ST_EUNSUPPORTED),
+    (dict(out=P), st.ST_EINVAL),                       # out aliases q
+    (dict(out=BIG + 8), st.ST_EALIGN),
+    # with the output projection
+    (dict(w_o=P4, c_out=0), st.ST_EINVAL),
+    (dict(w_o=P4, c_out=1150), st.ST_EUNSUPPORTED),    # c_out % 4
+    (dict(w_o=P4, c_out=1152, ws=None), st.ST_EWORKSPACE),
+    (dict(w_o=P4, c_out=1152, ws=2 * BIG, ws_bytes=100), st.ST_EWORKSPACE),
+    (dict(w_o=P4 + 8, c_out=1152, ws=2 * BIG, ws_bytes=1 << 40), st.ST_EALIGN),
+    (dict(w_o=P4, c_out=1152, ws=BIG + 64, ws_bytes=1 << 40), st.ST_EINVAL),   # workspace overlaps out
+    (dict(w_o=P4, c_out=1152, ws=P2, ws_bytes=1 << 40), st.ST_EINVAL),         # workspace overlaps k
 ])
-def test_attn_spatial_validation(args, want):
-    assert code(st.st_attn_spatial, *args) == want
+def test_attn_spatial_validation(kw, want):
+    assert code(st.st_attn_spatial, *attn_args(**kw)) == want
+
+
+def test_attn_workspace():
+    assert st.st_attn_workspace(ROWS, 16, 72, st.ST_BF16) == ROWS * 16 * 72 * 2
+    assert st.st_attn_workspace(10, 2, 64, st.ST_F32) == 5120
+    assert st.st_attn_workspace(-1, 2, 64, st.ST_F32) == 0
 
 
 @pytest.mark.parametrize("t_valid,want", [(0, st.ST_EINVAL), (53, st.ST_EINVAL)])
 def test_attn_temporal_validation(t_valid, want):
-    assert code(st.st_attn_temporal, P, P2, P3, 1, 8160, 52, t_valid, 16, 72, 0.1, st.ST_BF16, BIG) == want
+    assert code(st.st_attn_temporal, P, P2, P3, 1, 8160, 52, t_valid, 16, 72, 0.1, st.ST_BF16, None, 0, BIG, None,
+                0) == want
 
 
 def chunk_args(**kw):
@@ -295,3 +320,21 @@ def test_block_noalloc_rejects_beyond_its_scratch_before_any_gpu_work():
     assert code(st.st_block_sliced_noalloc, *args) == st.ST_EWORKSPACE
     args[2] = 25                                                       # T % n_t
     assert code(st.st_block_sliced_noalloc, *args) == st.ST_EINVAL
+
+
+def test_a2a_validation():
+    args = dict(x=P, send=BIG, dir=st.ST_A2A_S2T, B=1, T=56, S=8160, C_=1152, P=8, elem_bytes=2)
+
+    def c(fn, **kw):
+        a = dict(args)
+        a.update(kw)
+        return code(fn, *a.values())
+    for fn in (st.st_a2a_pack, st.st_a2a_unpack):
+        assert c(fn, x=None) == st.ST_EINVAL
+        assert c(fn, dir=2) == st.ST_EINVAL
+        assert c(fn, T=51) == st.ST_EINVAL                      # T % P
+        assert c(fn, S=8161) == st.ST_EINVAL                    # S % P
+        assert c(fn, P=0) == st.ST_EINVAL
+        assert c(fn, elem_bytes=3) == st.ST_EINVAL
+        assert c(fn, x=P + 1) == st.ST_EALIGN
+        assert c(fn, send=P + 64) == st.ST_EINVAL               # overlapping buffers

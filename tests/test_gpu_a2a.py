@@ -1,7 +1,7 @@
 """Local pack / unpack around the P-way all-to-all, on the GPU against the oracle's exchange.
 
 All P ranks are emulated on one GPU: each rank packs its shard with the library
-(st_relayout), the collective's block transpose is stood in for by plain device
+(st_a2a_pack), the collective's block transpose is stood in for by plain device
 copies (recv[q][r] = send[r][q]), and each rank unpacks.  Every element must
 land where the oracle's all-to-all puts it (bit-exact), in both directions, up
 to the 1080p per-GPU shape at P = 8 (T padded to 56 frames, 1020 patches per
@@ -44,12 +44,12 @@ def test_pack_exchange_unpack_matches_oracle(B, T, S, C, P, dt):
     sends = []
     for r in range(P):
         send = t_.empty((P, B, tp, sp, C), dtype=dev_s[r].dtype, device="cuda")
-        a2a.pack_s2t(dev_s[r], send, B, T, sp, C, P)
+        a2a.pack_s2t(dev_s[r], send, B, T, S, C, P)
         sends.append(send)
     frames = []
     for q, recv in enumerate(exchange(sends)):
         y = t_.empty((B, tp, S, C), dtype=recv.dtype, device="cuda")
-        a2a.unpack_s2t(recv, y, B, T, sp, C, P)
+        a2a.unpack_s2t(recv, y, B, T, S, C, P)
         frames.append(y)
     t_.cuda.synchronize()
     want_t = oracle.a2a_s_to_t(shards_s)

@@ -344,7 +344,7 @@ def test_4096px_image_attention_sampled():
     q, k, v, o = (empty((S, H, d)) for _ in range(4))
     st.st_qkv_norm_rope(xd, S, C, wq, g, g, EPS, 1.0, st.ST_ROPE_2D, tab, npos, None, S, 0, grid_w, H, d, st.ST_BF16, q, k,
                         v)
-    st.st_attn_spatial(q, k, v, 1, 1, S, H, d, 1 / math.sqrt(d), st.ST_BF16, o)
+    st.st_attn_spatial(q, k, v, 1, 1, S, H, d, 1 / math.sqrt(d), st.ST_BF16, None, 0, o)
     y = empty((S, C))
     st.st_out_proj(o, S, H * d, wo, C, st.ST_BF16, y)
     t_.cuda.synchronize()

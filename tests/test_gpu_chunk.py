@@ -93,7 +93,7 @@ def test_attn_chunk_without_lse_path_matches_spatial_kernel():
     q, k, v = (to_dev(a) for a in tensors((outer, L, H, d), (outer, L, H, d), 901, BF))
     a, b = empty((outer, L, H, d)), empty((outer, L, H, d))
     st.st_attn_chunk(q, k, v, outer, L, L, L, H, d, 1 / math.sqrt(d), BF, a, lse_buf(outer, H, L))
-    st.st_attn_spatial(q, k, v, 1, outer, L, H, d, 1 / math.sqrt(d), BF, b)
+    st.st_attn_spatial(q, k, v, 1, outer, L, H, d, 1 / math.sqrt(d), BF, None, 0, b)
     sync()
     assert t_.equal(a, b)
 

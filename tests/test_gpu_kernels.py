@@ -279,7 +279,7 @@ def test_attn_spatial(B, T, S, H, d, q_std, dt):
     q, k, v = qkv_tensors((B, T, S, H, d), 31 + S + d, dt, q_std)
     out = empty((B, T, S, H, d), dt == BF)
     scale = 1.0 / math.sqrt(d)
-    st.st_attn_spatial(to_dev(q), to_dev(k), to_dev(v), B, T, S, H, d, scale, dt, out)
+    st.st_attn_spatial(to_dev(q), to_dev(k), to_dev(v), B, T, S, H, d, scale, dt, None, 0, out)
     sync()
     ref = oracle.attn_spatial(f64(q), f64(k), f64(v), scale)
     assert_close(f64(out), ref, bf16=dt == BF, what="O")
@@ -324,7 +324,7 @@ def test_attn_spatial_peaked_scores(T, S, H, d, prescaled):
         q = st_synth.f32_to_bf16_bits((f64(q) * (scale * math.log2(math.e))).astype(np.float32))
         scale = math.log(2.0)
     out = empty(shape)
-    st.st_attn_spatial(to_dev(q), to_dev(k), to_dev(v), 1, T, S, H, d, scale, BF, out)
+    st.st_attn_spatial(to_dev(q), to_dev(k), to_dev(v), 1, T, S, H, d, scale, BF, None, 0, out)
     sync()
     ref = oracle.attn_spatial(f64(q), f64(k), f64(v), scale)
     ma, rl = assert_close(f64(out), ref, True, "O")
@@ -336,7 +336,7 @@ def test_attn_temporal(B, S, T, tv, H, d, dt):
     q, k, v = qkv_tensors((B, S, T, H, d), 41 + T + S, dt)
     out = empty((B, S, T, H, d), dt == BF)
     scale = 1.0 / math.sqrt(d)
-    st.st_attn_temporal(to_dev(q), to_dev(k), to_dev(v), B, S, T, tv, H, d, scale, dt, out)
+    st.st_attn_temporal(to_dev(q), to_dev(k), to_dev(v), B, S, T, tv, H, d, scale, dt, None, 0, out)
     sync()
     ref = oracle.attn_temporal(f64(q), f64(k), f64(v), scale, tv)
     assert_close(f64(out), ref, bf16=dt == BF, what="O")
@@ -348,7 +348,40 @@ def test_attention_is_deterministic():
     outs = []
     for _ in range(3):
         o = empty((1, 2, 500, 2, 72))
-        st.st_attn_spatial(dq, dk, dv, 1, 2, 500, 2, 72, 1 / math.sqrt(72), BF, o)
+        st.st_attn_spatial(dq, dk, dv, 1, 2, 500, 2, 72, 1 / math.sqrt(72), BF, None, 0, o)
         outs.append(to_host(o))
     sync()
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
+
+
+@pytest.mark.parametrize("temporal,dt", [(False, BF), (True, BF), (False, F32), (True, F32)])
+def test_attention_with_output_projection(temporal, dt):
+    """w_o given: out = O . w_o^T, O staged in the caller's workspace; bit-identical to the
+    attention call followed by st_out_proj, and within the bars of the oracle's linear(attention)."""
+    bf = dt == BF
+    B, A, L, H, d, C = (1, 40, 52, 16, 72, 1152) if bf else (1, 6, 10, 2, 64, 128)
+    tv = L - 3 if temporal else L
+    q, k, v = qkv_tensors((B, A, L, H, d), 77 + L, dt)
+    w = st_synth.randn((C, H * d), 78, std=0.02, dtype="bf16" if bf else "f32")
+    qd, kd, vd, wd = to_dev(q), to_dev(k), to_dev(v), to_dev(w)
+    rows = B * A * L
+    nb = st.st_attn_workspace(rows, H, d, dt)
+    ws = t_.empty(nb, dtype=t_.uint8, device="cuda")
+    out = empty((rows, C), bf)
+    o, y2 = empty((B, A, L, H, d), bf), empty((rows, C), bf)
+    scale = 1.0 / math.sqrt(d)
+    if temporal:
+        st.st_attn_temporal(qd, kd, vd, B, A, L, tv, H, d, scale, dt, wd, C, out, ws, nb)
+        st.st_attn_temporal(qd, kd, vd, B, A, L, tv, H, d, scale, dt, None, 0, o)
+    else:
+        st.st_attn_spatial(qd, kd, vd, B, A, L, H, d, scale, dt, wd, C, out, ws, nb)
+        st.st_attn_spatial(qd, kd, vd, B, A, L, H, d, scale, dt, None, 0, o)
+    st.st_out_proj(o, rows, H * d, wd, C, dt, y2)
+    sync()
+    assert t_.equal(out, y2)
+    att = oracle.attn_temporal(f64(q), f64(k), f64(v), scale, tv) if temporal else \
+        oracle.attn_spatial(f64(q), f64(k), f64(v), scale)
+    # the projection's input is the attention output as stored (bf16 or fp32)
+    ref = oracle.linear(f64(o).reshape(rows, H * d), f64(w))
+    assert_close(f64(out), ref, bf, "O w_o^T")
+    assert_close(f64(o), att, bf, "O")
