@@ -11,10 +11,11 @@ its rows back in [B,T,S,C] order.  Inputs are seeded synthetic tensors
 already resident in HBM.
 
 The JSON line reports the whole-step throughput in algorithmic TFLOP/s, each
-kernel's average duration from HIP events recorded on the launch stream, the
+kernel's median duration from HIP events recorded on the launch stream, the
 same step with the two relayouts as separate passes (bit-identical result),
-the standalone relayout rate next to a same-run device-to-device copy of the
-same bytes, a
+the standalone relayout rate next to a same-run device-to-device copy and a
+plain streaming copy of the same bytes, the QKV projection with and without its
+norm/RoPE epilogue, the same layer pair at the 720p 4 s shape, a
 roofline entry for the dominant kernel (spatial attention; its HBM traffic
 comes from the committed rocprofv3 counter summary when that summary matches
 the kernel source), the slicing schedule's time (N_T = N_S = 4, T padded to
@@ -83,42 +84,69 @@ def flops_and_bytes(B, T, S, C, H, d):
     return f, by
 
 
-def cpu_baseline(inp, cfg, budget_s=20.0):
-    """The fp64 oracle, as it stands, on a bounded sample of the same workload.
+def _oracle_attention_task(args):
+    """One (frame, head) sequence of the spatial layer's attention, single-threaded BLAS."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    q, k, v, scale = args
+    with threadpool_limits(1):
+        return oracle.attention(q, k, v, scale)
 
-    Sample: the spatial layer on whole frames (all 16 heads, all 8160 patches),
-    one frame at a time until the time budget is reached, plus the temporal
-    layer on 160 patches x all frames.  Throughput = algorithmic flops of the
-    sample / wall time.
+
+def cpu_baseline(cfg_id):
+    """The fp64 oracle, as it stands, on a fixed sample of the same workload, on the host's cores.
+
+    Sample: the spatial layer on frames {0, T/2, T-1} (all heads, all patches) and the temporal
+    layer on 160 patches x all frames.  The attention of each (frame, head) sequence -- nearly all
+    of the work -- runs in a pool of one single-threaded worker per host core; the projections and
+    the temporal layer run in this process with the BLAS library's threads.  Throughput =
+    algorithmic flops of the sample / wall time.  Runs before the GPU is touched (the pool's
+    workers are fresh interpreters).
     """
+    import multiprocessing as mp
+
     import oracle
     import st_synth
     from threadpoolctl import threadpool_info
 
+    inp = st_synth.make_inputs(cfg_id)
+    cfg = inp["cfg"]
     B, T, S, C, H, d, gw = cfg["B"], cfg["T"], cfg["S"], cfg["C"], cfg["H"], cfg["d"], cfg["grid_w"]
     eps, base = st_synth.EPS, st_synth.ROPE_BASE
     ws = dict(w_qkv=st_synth.to_f64(inp["w_qkv_s"]), w_o=st_synth.to_f64(inp["w_o_s"]),
               g_q=inp["g_q"].astype(np.float64), g_k=inp["g_k"].astype(np.float64))
     wt = dict(w_qkv=st_synth.to_f64(inp["w_qkv_t"]), w_o=st_synth.to_f64(inp["w_o_t"]),
               g_q=inp["g_q"].astype(np.float64), g_k=inp["g_k"].astype(np.float64))
-    hd = H * d
-    flops, frames = 0.0, 0
+    hd, scale = H * d, 1.0 / math.sqrt(d)
+    frames = sorted({0, T // 2, T - 1})
+    cores = len(os.sched_getaffinity(0))
+    pool = mp.get_context("spawn").Pool(cores)
+    pool.map(_oracle_attention_task, [(np.zeros((2, d)),) * 3 + (scale,)] * cores)   # workers up and imported
     t0 = time.perf_counter()
-    while frames < T and time.perf_counter() - t0 < budget_s / 2:
-        x = st_synth.to_f64(inp["x"][:, frames:frames + 1])
-        oracle.spatial_layer(x, ws, H, d, gw, eps, base)
-        flops += 2.0 * S * C * 3 * hd + 4.0 * S * S * d * H + 2.0 * S * hd * C
-        frames += 1
+    pos = np.tile(oracle.positions_2d(S, gw), (B, 1))
+    tasks, qkv_flops = [], 0.0
+    for t in frames:
+        x = st_synth.to_f64(inp["x"][:, t]).reshape(B * S, C)
+        q, k, v = oracle.qkv_norm_rope(x, ws["w_qkv"], ws["g_q"], ws["g_k"], eps, H, d, "2d", pos, base)
+        tasks += [(q[:, h], k[:, h], v[:, h], scale) for h in range(H)]
+    outs = pool.map(_oracle_attention_task, tasks, chunksize=1)
+    for f in range(len(frames)):   # the output projection of each frame's attention output
+        o = np.stack(outs[f * H:(f + 1) * H], axis=1).reshape(B * S, hd)
+        oracle.linear(o, ws["w_o"])
+    flops = len(frames) * (2.0 * S * C * 3 * hd + 4.0 * S * S * d * H + 2.0 * S * hd * C)
     P = 160
     xt = oracle.bt_to_bs(st_synth.to_f64(inp["x"][:, :, :P]))
     oracle.temporal_layer(xt, wt, H, d, eps, base)
     flops += 2.0 * P * T * C * 3 * hd + 4.0 * T * T * d * H * P + 2.0 * P * T * hd * C
     dt = time.perf_counter() - t0
+    pool.close()
+    pool.join()
     threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"spatial layer on {frames} whole frame(s) (8160 patches x 16 heads) + temporal layer on "
-                      f"{P} patches x {T} frames; fp64 numpy, {dt:.1f} s wall",
-            "seconds": round(dt, 2), "host_cores_visible": len(os.sched_getaffinity(0))}
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"spatial layer on frames {frames} (all {S} patches x {H} heads; attention per (frame, head) "
+                      f"in a pool of {cores} single-threaded workers, projections on {threads} BLAS threads) + "
+                      f"temporal layer on {P} patches x {T} frames; fp64 numpy, {dt:.1f} s wall",
+            "seconds": round(dt, 2), "host_cores_visible": cores}
 
 
 def time_slicing(x, wsd, wtd, B, T, S, gw, C, H, d, stream, reps):
@@ -346,33 +374,28 @@ def time_chunked_attention(lp, B, T, S, H, d, reps, stream, n_chunks=4):
             "merge_frac_hbm_peak": round(merge_bytes / times["merge"] / 1e6 / PEAK_HBM_GBS, 4)}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="1080p", choices=sorted(WORKLOADS))
-    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--no-sliced", action="store_true", help="skip timing the slicing schedule")
-    ap.add_argument("--no-chunked", action="store_true", help="skip timing chunked attention + merges")
-    ap.add_argument("--no-a2a", action="store_true", help="skip timing the all-to-all pack/unpack")
-    ap.add_argument("--no-vchange", action="store_true", help="skip timing the V-Major change detection")
-    ap.add_argument("--no-image", action="store_true", help="skip timing attention at the 4096px image shape")
-    ap.add_argument("--cpu-budget", type=float, default=20.0)
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); it has no multi-GPU mode",
-              file=sys.stderr)
-        sys.exit(2)
+def median_ms(fn, reps, stream):
+    """Median of `reps` single-call durations, HIP events on the launch stream, after one warm-up call."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
 
+
+def time_layer_pair(cfg_id, steps, warmup, stream):
+    """The unsliced layer pair of one workload, step by step through the C ABI: per-kernel medians of HIP
+    events on the launch stream, and the wall time per step bracketed by synchronize on both sides."""
     import torch
 
     import st_synth
-    import temporal_attention_amd as st
     from temporal_attention_amd.pipeline import LayerPair
 
-    torch.cuda.set_device(0)
-    cfg_id = WORKLOADS[args.workload]
     inp = st_synth.make_inputs(cfg_id)
     cfg = inp["cfg"]
     B, T, S, C, H, d, gw = cfg["B"], cfg["T"], cfg["S"], cfg["C"], cfg["H"], cfg["d"], cfg["grid_w"]
@@ -387,32 +410,26 @@ def main():
                g_k=torch.from_numpy(inp["g_k"]).cuda())
     lp = LayerPair(B, T, S, gw, C, H, d)
     lp.set_weights(wsd, wtd)
-    steps = lp.steps(x)
-    names = [n for n, _ in steps]
-
-    for _ in range(args.warmup):
-        for _, fn in steps:
+    lsteps = lp.steps(x)
+    names = [n for n, _ in lsteps]
+    for _ in range(warmup):
+        for _, fn in lsteps:
             fn()
     torch.cuda.synchronize()
-
-    stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(steps) + 1)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(lsteps) + 1)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         ev[i][0].record(stream)
-        for j, (_, fn) in enumerate(steps):
+        for j, (_, fn) in enumerate(lsteps):
             fn()
             ev[i][j + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = {n: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
+    per = {n: float(np.median([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)]))
            for j, n in enumerate(names)}
-    step_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][-1]) for i in range(args.steps)]))
-    ms_per_step = wall * 1e3 / args.steps   # bracketed by synchronize on both sides
-
+    step_ms = float(np.median([ev[i][0].elapsed_time(ev[i][-1]) for i in range(steps)]))
     fl, by = flops_and_bytes(B, T, S, C, H, d)
-    total_flops = sum(fl.values())
     kernels = {}
     for n in names:
         e = {"ms": round(per[n], 4)}
@@ -423,6 +440,45 @@ def main():
             e["gbs"] = round(by[n] / per[n] / 1e6, 1)
             e["frac_hbm_peak"] = round(by[n] / per[n] / 1e6 / PEAK_HBM_GBS, 4)
         kernels[n] = e
+    res = {"per": per, "kernels": kernels, "flops": fl, "bytes": by, "ms_per_step": wall * 1e3 / steps,
+           "step_ms_median": step_ms}
+    return lp, x, wsd, wtd, inp, cfg, res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="1080p", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-sliced", action="store_true", help="skip timing the slicing schedule")
+    ap.add_argument("--no-chunked", action="store_true", help="skip timing chunked attention + merges")
+    ap.add_argument("--no-a2a", action="store_true", help="skip timing the all-to-all pack/unpack")
+    ap.add_argument("--no-vchange", action="store_true", help="skip timing the V-Major change detection")
+    ap.add_argument("--no-image", action="store_true", help="skip timing attention at the 4096px image shape")
+    ap.add_argument("--no-720p", action="store_true", help="skip the 720p layer-pair row")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); it has no multi-GPU mode",
+              file=sys.stderr)
+        sys.exit(2)
+
+    cfg_id = WORKLOADS[args.workload]
+    cpu = None if args.no_cpu else cpu_baseline(cfg_id)   # before the GPU is touched
+
+    import torch
+
+    import temporal_attention_amd as st
+    from temporal_attention_amd.pipeline import LayerPair
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    lp, x, wsd, wtd, inp, cfg, res = time_layer_pair(cfg_id, args.steps, args.warmup, stream)
+    B, T, S, C, H, d, gw = cfg["B"], cfg["T"], cfg["S"], cfg["C"], cfg["H"], cfg["d"], cfg["grid_w"]
+    per, kernels, fl, by = res["per"], res["kernels"], res["flops"], res["bytes"]
+    ms_per_step, step_ms = res["ms_per_step"], res["step_ms_median"]
+    total_flops = sum(fl.values())
     attn_achieved = fl["attn_spatial"] / per["attn_spatial"] / 1e9
 
     # The step stores both relayouts from the output projections.  The same step with separate
@@ -439,33 +495,38 @@ def main():
     unfused_ms = (time.perf_counter() - u0) * 1e3 / args.steps
     rl = {}
     for name, fn in unfused:
-        if not name.startswith("relayout"):
-            continue
-        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        r0.record(stream)
-        for _ in range(args.steps):
-            fn()
-        r1.record(stream)
-        torch.cuda.synchronize()
-        rl[name] = r0.elapsed_time(r1) / args.steps
-        kernels[name + "_standalone"] = {"ms": round(rl[name], 4), "gbs": round(by[name] / rl[name] / 1e6, 1),
-                                         "frac_hbm_peak": round(by[name] / rl[name] / 1e6 / PEAK_HBM_GBS, 4)}
+        if name.startswith("relayout"):
+            rl[name] = median_ms(fn, max(5, args.steps), stream)
+            kernels[name + "_standalone"] = {"ms": round(rl[name], 4), "gbs": round(by[name] / rl[name] / 1e6, 1),
+                                             "frac_hbm_peak": round(by[name] / rl[name] / 1e6 / PEAK_HBM_GBS, 4)}
     relayout_ms = rl["relayout_fwd"] + rl["relayout_bwd"]
     relayout_gbs = (by["relayout_fwd"] + by["relayout_bwd"]) / relayout_ms / 1e6
 
-    # practical ceiling of a relayout: a plain device-to-device copy of the same bytes, same run
+    # ceilings of a relayout, same run: torch's device-to-device copy of the same bytes, and a plain
+    # contiguous copy by the relayout kernel itself (identity strides: one lane per 16 bytes)
     cp_dst = torch.empty_like(x)
-    for _ in range(3):
-        cp_dst.copy_(x)
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record(stream)
-    for _ in range(args.steps):
-        cp_dst.copy_(x)
-    c1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbs = by["relayout_fwd"] / (c0.elapsed_time(c1) / args.steps) / 1e6
+    copy_gbs = by["relayout_fwd"] / median_ms(lambda: cp_dst.copy_(x), max(5, args.steps), stream) / 1e6
+    n_el = x.numel()
+    stream_ms = median_ms(lambda: st.st_relayout(x, [1], cp_dst, [1], [n_el], 1, 2), max(5, args.steps), stream)
+    stream_gbs = by["relayout_fwd"] / stream_ms / 1e6
     del cp_dst
     traffic = measured_traffic()
+
+    # The QKV projection with and without its RMSNorm + RoPE epilogue: the plain projection of the
+    # same shape is st_out_proj with the 3*H*d output rows of w_qkv.  The difference is what the
+    # fused norm costs; done as its own pass it would move 4*N*H*d*2 bytes (read q, k; write q, k).
+    N, hd = B * T * S, H * d
+    plain = torch.empty((N, 3 * hd), dtype=torch.bfloat16, device="cuda")
+    qkv_plain_ms = median_ms(lambda: st.st_out_proj(x, N, C, wsd["w_qkv"], 3 * hd, st.ST_BF16, plain),
+                             max(5, args.steps), stream)
+    del plain
+    norm_bytes = 4.0 * N * hd * 2
+    epilogue = {"qkv_with_norm_rope_ms": round(per["qkv_spatial"], 4), "qkv_plain_ms": round(qkv_plain_ms, 4),
+                "fused_norm_rope_ms": round(per["qkv_spatial"] - qkv_plain_ms, 4),
+                "standalone_norm_rope_bytes": int(norm_bytes),
+                "standalone_norm_rope_ms_at_stream_rate": round(norm_bytes / (stream_gbs * 1e6), 4),
+                "note": "a separate norm/RoPE pass would read and write q and k once (at the same-run streaming "
+                        "copy rate); fused into the projection epilogue it moves no extra HBM bytes"}
 
     out = {
         "metric": METRIC,
@@ -489,8 +550,11 @@ def main():
         "relayout_gbs": round(relayout_gbs, 1),
         "relayout_frac_hbm_peak": round(relayout_gbs / PEAK_HBM_GBS, 4),
         "device_copy_gbs": round(copy_gbs, 1),
-        "relayout_frac_of_device_copy": round(relayout_gbs / copy_gbs, 4),
+        "streaming_copy_gbs": round(stream_gbs, 1),
+        "relayout_frac_of_streaming_copy": round(relayout_gbs / stream_gbs, 4),
+        "timing": "per-kernel figures are medians over the timed steps of HIP events on the launch stream",
         "kernels": kernels,
+        "qkv_epilogue": epilogue,
         "roofline": {"kernel": "attn_long_kernel<72,2> (spatial attention)", "bound": "mfma",
                      "achieved": round(attn_achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_achieved / PEAK_BF16_TFLOPS, 4),
@@ -499,13 +563,30 @@ def main():
                      "algorithmic_bytes": round(4.0 * B * T * S * H * d * 2 / 1e9, 4)},
     }
 
+    if cfg_id != 2 and not args.no_720p:
+        # the 720p 4 s workload (B=1, T=24, S=3600 on 80x45), same launch sequence, medians
+        del lp
+        torch.cuda.empty_cache()
+        lp2, x2, _, _, _, cfg2, r2 = time_layer_pair(2, args.steps, args.warmup, stream)
+        tf2 = sum(r2["flops"].values())
+        out["workload_720p"] = {"config": {k: cfg2[k] for k in ("B", "T", "S", "C", "H", "d", "grid_w")},
+                                "ms_per_step": round(r2["ms_per_step"], 4),
+                                "tflops": round(tf2 / r2["ms_per_step"] / 1e9, 1),
+                                "kernels": r2["kernels"]}
+        del lp2, x2
+        torch.cuda.empty_cache()
+        lp = LayerPair(B, T, S, gw, C, H, d)
+        lp.set_weights(wsd, wtd)
+        for _, fn in lp.steps(x):
+            fn()
+
     if not args.no_sliced:
         out["sliced"], out["slicing_sweep"] = time_slicing(x, wsd, wtd, B, T, S, gw, C, H, d, stream,
                                                            max(2, args.steps // 5))
         torch.cuda.empty_cache()
 
     if not args.no_chunked:
-        steps[0][1]()   # the spatial layer's q, k, v again (the timed steps end on the temporal layer)
+        lp.steps(x)[0][1]()   # the spatial layer's q, k, v again (the timed steps end on the temporal layer)
         out["chunked_attention"] = time_chunked_attention(lp, B, T, S, H, d, max(2, args.steps // 2), stream)
 
     if not args.no_vchange:
@@ -517,8 +598,8 @@ def main():
     if not args.no_image:
         out["attn_image_4096px"] = time_image_attention(max(3, args.steps // 2), stream)
 
-    if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_budget)
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
 
 
