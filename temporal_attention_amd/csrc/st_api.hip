@@ -239,6 +239,7 @@ st_status check_block(const void *x, int B, int T, int t_valid, int S, int grid_
   if (dtype == ST_BF16 && (C % 64 || (H * d) % 64)) return ST_EUNSUPPORTED;
   if (C % 4) return ST_EUNSUPPORTED;
   if ((int64_t)B * T * S >= (1ll << 32) / 2) return ST_EUNSUPPORTED;
+  if ((int64_t)3 * H * d * C >= (1ll << 31)) return ST_EUNSUPPORTED;   // 32-bit weight offsets
   for (const st_layer_weights *w : {spatial, temporal})
     for (const void *p : {w->w_qkv, w->w_o, (const void *)w->g_q, (const void *)w->g_k})
       if (!aligned16(p)) return ST_EALIGN;
@@ -455,7 +456,8 @@ st_status st_qkv_norm_rope(const void *x, int64_t rows, int c_in, const void *w_
   if (dtype == ST_BF16 && c_in % 64) return ST_EUNSUPPORTED;
   const st_status rs = check_rope(rope_kind, rope_table, rope_npos, pos, pos_period, pos_offset, grid_w, d, rows);
   if (rs != ST_OK) return rs;
-  if ((int64_t)H * d * 3 >= (1 << 30) || rows >= (1ll << 40)) return ST_EUNSUPPORTED;
+  // the projection kernels index the weight matrix with 32-bit offsets
+  if ((int64_t)H * d * 3 * c_in >= (1ll << 31) || rows >= (1ll << 40)) return ST_EUNSUPPORTED;
   for (const void *p : {x, w_qkv, (const void *)g_q, (const void *)g_k, (const void *)q, (const void *)k,
                         (const void *)v})
     if (!aligned16(p)) return ST_EALIGN;
@@ -478,7 +480,7 @@ st_status st_out_proj(const void *a, int64_t rows, int k_in, const void *w, int 
   if (!dtype_ok(dtype)) return ST_EINVAL;
   if (!a || !w || !y || rows < 0 || k_in < 1 || n_out < 1) return ST_EINVAL;
   if (n_out % 4 || (dtype == ST_BF16 && k_in % 64)) return ST_EUNSUPPORTED;
-  if (rows >= (1ll << 40) || (int64_t)k_in * n_out >= (1ll << 40)) return ST_EUNSUPPORTED;
+  if (rows >= (1ll << 40) || (int64_t)k_in * n_out >= (1ll << 31)) return ST_EUNSUPPORTED;
   if (!aligned16(a) || !aligned16(w) || !aligned16(y)) return ST_EALIGN;
   const size_t e = esize(dtype);
   const Range ry = rng(y, rows * n_out * e);
@@ -492,7 +494,7 @@ st_status st_out_proj_relayout(const void *a, int64_t rows, int k_in, const void
   if (!dtype_ok(dtype)) return ST_EINVAL;
   if (!a || !w || !y || k_in < 1 || n_out < 1) return ST_EINVAL;
   if (n_out % 4 || (dtype == ST_BF16 && k_in % 64)) return ST_EUNSUPPORTED;
-  if (rows >= (1ll << 40) || (int64_t)k_in * n_out >= (1ll << 40)) return ST_EUNSUPPORTED;
+  if (rows >= (1ll << 40) || (int64_t)k_in * n_out >= (1ll << 31)) return ST_EUNSUPPORTED;
   if (!aligned16(a) || !aligned16(w) || !aligned16(y)) return ST_EALIGN;
   const size_t e = esize(dtype);
   const Range ry = rng(y, rows * n_out * e);

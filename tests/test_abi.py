@@ -338,3 +338,12 @@ def test_a2a_validation():
         assert c(fn, elem_bytes=3) == st.ST_EINVAL
         assert c(fn, x=P + 1) == st.ST_EALIGN
         assert c(fn, send=P + 64) == st.ST_EINVAL               # overlapping buffers
+
+
+def test_weight_matrices_beyond_32_bit_offsets_are_unsupported():
+    """The projection kernels address the weight matrix with 32-bit offsets: N*K >= 2^31 is refused
+    on the host before any GPU work."""
+    assert code(st.st_out_proj, P, 10, 65536, P2, 32768, st.ST_BF16, BIG) == st.ST_EUNSUPPORTED
+    assert code(st.st_out_proj_relayout, P, 10, 65536, P2, 32768, st.ST_BF16, 2, 5, BIG) == st.ST_EUNSUPPORTED
+    assert code(st.st_qkv_norm_rope, *qkv_args(c_in=1 << 20, H=128, d=64, rope_kind=st.ST_ROPE_NONE)) == \
+        st.ST_EUNSUPPORTED
