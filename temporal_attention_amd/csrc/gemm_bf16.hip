@@ -84,6 +84,25 @@ struct Tile {
 // consecutive rows at one kc hit 8 disjoint bank quads.
 __device__ __forceinline__ int slot_of(int row, int kc) { return row * 8 + (kc ^ (row & 7)); }
 
+// Epilogue staging.  A lane's accumulators hold 4 consecutive channels of one
+// token, so stores straight from them write 32-byte pieces of 16 different
+// rows per instruction.  Instead each wave converts half of its tile (32 tokens
+// x WN channels) to bf16 into its own LDS slot, reads it back along the rows and
+// stores 16 bytes per lane: a store instruction then covers whole stretches of
+// 3.5 token rows.  The slots reuse the pipeline stages, free after the K loop,
+// and need no workgroup barrier (a wave reads back only what it wrote).  Rows of
+// RS = 144 bf16 (288 bytes, 72 banks) put the 8-byte writes of 8 consecutive
+// rows x 4 lane groups on 64 distinct banks.
+template <int CT>
+struct Staging {
+  static constexpr int WN = 16 * CT;
+  static constexpr int RS = WN == 128 ? 144 : WN;   // row stride in bf16
+  static constexpr int CH = WN / 8;                 // 16-byte chunks per token row
+  static constexpr int SLOT = 32 * RS;              // bf16 per wave slot
+  static_assert(RS * 2 % 32 == 0 && (RS * 2 / 4) % 64 == 8, "row stride must spread 8 rows over the banks");
+  static_assert(CH % 2 == 0, "a half tile is whole 64-lane rounds");
+};
+
 // Global -> LDS loads of one stage: 1 KB (8 whole rows) per wavefront
 // instruction, lane l of block b filling slot 64 b + l.  Each lane's element offset inside the K
 // window is fixed for the whole K loop and computed once; rows past M or N
@@ -156,7 +175,15 @@ __device__ __forceinline__ void gemm_step(const u16 *__restrict__ As, const u16 
 
 template <int CT, int D, typename TabPtr>
 __device__ __forceinline__ void epilogue_qkv(const GemmArgs &a, f32x4 (&acc)[CT][kTT], int64_t m0, int nw0, int wm,
-                                             int l16, int g4, TabPtr tab);
+                                             int lane, u16 *slot, const float *gains, TabPtr tab);
+
+// Orders a wave's LDS writes before its reads of other lanes' data (LDS executes
+// one wave's instructions in order; this only keeps the compiler from moving them).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 // Floats of the RoPE table (npos positions x pairs x {cos, sin}); 0 without RoPE.
 template <int D>
@@ -198,26 +225,39 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_bf16_kernel(GemmArgs a, uint
   dma.init(a, m0, n0, lane, wave);
   const u16 *xb = XMAP ? a.x : a.x + m0 * a.K;
   const int nk = a.K / kBK;
-  // MODE 1: the RoPE table moves into the stage the last K step leaves free
-  // (its loads overlap that step's MFMAs), so the epilogue's cos/sin reads are
-  // LDS reads instead of dependent global loads.  Tables larger than a stage
-  // are read from global memory.
+  // MODE 1: the gains and the RoPE table move into the stage the last K step
+  // leaves free (their loads overlap that step's MFMAs): [gains 1 KB][table]
+  // [wave 7's staging slot].  The epilogue then issues no global loads once its
+  // stores have started (a load's wait would also wait for those stores).
+  // Tables too large for the stage are read from global memory.
+  constexpr int kGainsU16 = 512;   // 1 KB: g_q then g_k, fp32
   int64_t tab_floats = 0;
   if constexpr (MODE == 1) tab_floats = rope_table_floats<D>(a.rope);
-  const bool tab_lds = tab_floats > 0 && tab_floats * 4 <= TL::STAGE * 2;
+  const int64_t tab_u16 = (tab_floats * 2 + 127) & ~int64_t(127);
+  const bool tab_lds = tab_floats > 0 && kGainsU16 + tab_u16 + Staging<CT>::SLOT <= TL::STAGE;
   dma.issue(lds, 0, xb, a.w, wave);
   wait_vmem_upto<0>();
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     u16 *cur = lds + (kt & 1) * TL::STAGE;
     u16 *nxt = lds + ((kt & 1) ^ 1) * TL::STAGE;
-    if (kt + 1 == nk && tab_lds) {
-      // 1 KB per wave instruction; the last block's lanes past the end re-read the last 16 bytes
-      const int blocks = (int)((tab_floats + 255) / 256);
-      for (int b = wave; b < blocks; b += TL::NWAVES) {
-        const int64_t f = min<int64_t>((int64_t)b * 256 + lane * 4, tab_floats - 4);
-        __builtin_amdgcn_global_load_lds(a.rope.table + f, (__attribute__((address_space(3))) void *)(nxt + b * 512),
-                                         16, 0, 0);
+    if constexpr (MODE == 1) {
+      if (kt + 1 == nk) {
+        static_assert(D <= 128, "g_q and g_k fill one 1 KB load");
+        if (wave == TL::NWAVES - 1) {   // lanes past 2 D re-read g_k's last 16 bytes into the gains block's tail
+          const float *g = lane < D / 4 ? a.g_q + 4 * lane : a.g_k + 4 * min(lane - D / 4, D / 4 - 1);
+          __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)nxt, 16, 0, 0);
+        }
+        if (tab_lds) {
+          // 1 KB per wave instruction; the last block's lanes past the end re-read the last 16 bytes
+          const int blocks = (int)((tab_floats + 255) / 256);
+          for (int b = wave; b < blocks; b += TL::NWAVES) {
+            const int64_t f = min<int64_t>((int64_t)b * 256 + lane * 4, tab_floats - 4);
+            __builtin_amdgcn_global_load_lds(a.rope.table + f,
+                                             (__attribute__((address_space(3))) void *)(nxt + kGainsU16 + b * 512), 16,
+                                             0, 0);
+          }
+        }
       }
     }
     gemm_step<CT, XMAP>(cur, cur + TL::LDS_A, nxt, kt + 1 < nk, (kt + 1) * kBK, dma, xb, a.w, wave, wn, wm, l16, g4,
@@ -227,8 +267,40 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_bf16_kernel(GemmArgs a, uint
   }
 
   // ------------------------------------------------------------------ epilogue
+  typedef Staging<CT> SG;
   const int nw0 = n0 + wn * TL::WN;   // first channel of this wave
   if constexpr (MODE == 0) {
+    if (a.N % 8 == 0 && (reinterpret_cast<uintptr_t>(a.y) & 15) == 0) {
+      static_assert(8 * SG::SLOT <= kStages * TL::STAGE, "wave slots fit the stages");
+      u16 *slot = lds + wave * SG::SLOT;
+      const int64_t rl = m0 + wm * kWM + lane;   // the lane's token row, mapped once
+      const int64_t roff = rl < a.M ? map_row(rl, a.ymap) * a.N : -1;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            const f32x4 &c = acc[ct][half * 2 + t2];
+            uint2 o;
+            o.x = pack_bf16x2(c[0], c[1]);
+            o.y = pack_bf16x2(c[2], c[3]);
+            *reinterpret_cast<uint2 *>(slot + (t2 * 16 + l16) * SG::RS + ct * 16 + g4 * 4) = o;
+          }
+        wave_lds_sync();
+#pragma unroll
+        for (int it = 0; it < SG::CH / 2; ++it) {
+          const int c = it * 64 + lane;
+          const int tok = c / SG::CH, ch = c - tok * SG::CH;
+          const int64_t ro = __shfl(roff, half * 32 + tok);
+          const uint4 v = *reinterpret_cast<const uint4 *>(slot + tok * SG::RS + ch * 8);
+          const int n = nw0 + ch * 8;
+          if (ro >= 0 && n < a.N) *reinterpret_cast<uint4 *>(a.y + ro + n) = v;
+        }
+        wave_lds_sync();
+      }
+      return;
+    }
 #pragma unroll
     for (int tt = 0; tt < kTT; ++tt) {
       const int64_t r = m0 + wm * kWM + tt * 16 + l16;
@@ -245,44 +317,91 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_bf16_kernel(GemmArgs a, uint
       }
     }
   } else {
+    // Wave slots: waves 0-6 in the other stage, wave 7 after the gains and table.
+    static_assert(7 * SG::SLOT <= TL::STAGE, "seven wave slots fit one stage");
+    static_assert(kGainsU16 + SG::SLOT <= TL::STAGE, "gains and one slot fit one stage");
+    u16 *tstage = lds + (nk & 1) * TL::STAGE;
+    u16 *slot = wave < 7 ? lds + ((nk & 1) ^ 1) * TL::STAGE + wave * SG::SLOT
+                         : tstage + kGainsU16 + (tab_lds ? tab_u16 : 0);
+    const float *gl = reinterpret_cast<const float *>(tstage);
     if (tab_lds) {
-      const float *t = reinterpret_cast<const float *>(lds + (nk & 1) * TL::STAGE);   // the last step's free stage
-      epilogue_qkv<CT, D>(a, acc, m0, nw0, wm, l16, g4, t);
+      epilogue_qkv<CT, D>(a, acc, m0, nw0, wm, lane, slot, gl, reinterpret_cast<const float *>(tstage + kGainsU16));
     } else {
-      epilogue_qkv<CT, D>(a, acc, m0, nw0, wm, l16, g4, a.rope.table);
+      epilogue_qkv<CT, D>(a, acc, m0, nw0, wm, lane, slot, gl, a.rope.table);
     }
   }
 }
 
-// MODE 1 epilogue: the wave's channels are HPW whole heads.
+// MODE 1 epilogue: the wave's channels are HPW whole heads; the results go out
+// through the wave's slot (Staging), half a tile at a time.
 template <int CT, int D, typename TabPtr>
 __device__ __forceinline__ void epilogue_qkv(const GemmArgs &a, f32x4 (&acc)[CT][kTT], int64_t m0, int nw0, int wm,
-                                             int l16, int g4, TabPtr tab) {
+                                             int lane, u16 *slot, const float *gains, TabPtr tab) {
   typedef Tile<CT> TL;
+  typedef Staging<CT> SG;
   constexpr int HPW = TL::WN / D;
   static_assert(TL::WN % D == 0, "wave channel range must hold whole heads");
+  static_assert(D % 8 == 0, "a 16-byte chunk must not straddle two heads");
+  const int l16 = lane & 15, g4 = lane >> 4;
   const int H = a.H;
   const int hd = H * D;
   const int gh0 = nw0 / D;   // global head index (over 3H) of the wave's first head
   const int npairs = a.rope.kind == ST_ROPE_2D ? D / 4 : D / 2;
 
+  // Where each head of the wave starts in q, k or v (wave-uniform), and whether it exists.
+  u16 *hbase[HPW];
+  bool hok[HPW];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    const int gh = gh0 + hh, which = gh / H;
+    hok[hh] = gh < 3 * H;
+    hbase[hh] = (which == 0 ? a.q : (which == 1 ? a.k : a.v)) + (gh - which * H) * D;
+  }
+  // Stores half `half` of the wave's tile from its slot: chunk c of the half is
+  // 8 channels of token row c / CH, inside one head.
+  auto flush = [&](auto half_c) {
+    constexpr int half = decltype(half_c)::value;
+    wave_lds_sync();
+#pragma unroll
+    for (int it = 0; it < SG::CH / 2; ++it) {
+      const int c = it * 64 + lane;
+      const int tok = c / SG::CH, ch = c - tok * SG::CH;
+      const int cl = ch * 8, hh = cl / D;
+      const int64_t r = m0 + wm * kWM + half * 32 + tok;
+      const uint4 v = *reinterpret_cast<const uint4 *>(slot + tok * SG::RS + cl);
+      u16 *base = hbase[0];
+      bool ok = hok[0];
+#pragma unroll
+      for (int h2 = 1; h2 < HPW; ++h2) {
+        base = hh == h2 ? hbase[h2] : base;
+        ok = hh == h2 ? hok[h2] : ok;
+      }
+      if (r < a.M && ok) *reinterpret_cast<uint4 *>(base + r * hd + (cl - hh * D)) = v;
+    }
+    wave_lds_sync();
+  };
+  auto put = [&](int t2, int ct, const uint2 &o) {
+    *reinterpret_cast<uint2 *>(slot + (t2 * 16 + l16) * SG::RS + ct * 16 + g4 * 4) = o;
+  };
+
+  typedef std::integral_constant<int, 0> H0;
+  typedef std::integral_constant<int, 1> H1;
+
   // A wave whose heads are all v heads stores the projection as it is.
   if (gh0 / H == 2 && (gh0 + HPW - 1) / H == 2) {
+    auto half_v = [&](auto half_c) {
+      constexpr int half = decltype(half_c)::value;
 #pragma unroll
-    for (int tt = 0; tt < kTT; ++tt) {
-      const int64_t r = m0 + wm * kWM + tt * 16 + l16;
-      if (r >= a.M) continue;
+      for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        const int cl = ct * 16 + g4 * 4;
-        const int gh = gh0 + cl / D;
-        if (gh >= 3 * H) continue;
-        uint2 o;
-        o.x = pack_bf16x2(acc[ct][tt][0], acc[ct][tt][1]);
-        o.y = pack_bf16x2(acc[ct][tt][2], acc[ct][tt][3]);
-        *reinterpret_cast<uint2 *>(a.v + r * hd + (gh - 2 * H) * D + (cl - (cl / D) * D)) = o;
-      }
-    }
+        for (int ct = 0; ct < CT; ++ct) {
+          const f32x4 &c = acc[ct][half * 2 + t2];
+          put(t2, ct, uint2{pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3])});
+        }
+      flush(half_c);
+    };
+    half_v(H0{});
+    half_v(H1{});
     return;
   }
 
@@ -292,7 +411,6 @@ __device__ __forceinline__ void epilogue_qkv(const GemmArgs &a, f32x4 (&acc)[CT]
   // share the token (lane groups 16 apart).
   float inv[kTT][HPW];
   int p0[kTT], p1[kTT];
-  int64_t roff[kTT];         // element offset of the lane's token row in q, k, v; -1: past the last row
   const uint32_t period = (uint32_t)min<int64_t>(a.rope.period, 1ll << 30);
   const uint32_t base_i = a.rope.kind == ST_ROPE_NONE ? 0u : (uint32_t)(m0 % a.rope.period);   // one per workgroup
 #pragma unroll
@@ -316,7 +434,6 @@ __device__ __forceinline__ void epilogue_qkv(const GemmArgs &a, f32x4 (&acc)[CT]
       inv[tt][hh] = rsqrtf(ss[hh] * (1.0f / D) + a.eps);
     }
     const int64_t r = m0 + wm * kWM + tt * 16 + l16;
-    roff[tt] = r < a.M ? r * hd : -1;
     p0[tt] = p1[tt] = 0;
     if (a.rope.kind != ST_ROPE_NONE) {
       if (a.rope.pos) {   // caller's positions, clamped into the table (out-of-range positions are undefined)
@@ -335,13 +452,15 @@ __device__ __forceinline__ void epilogue_qkv(const GemmArgs &a, f32x4 (&acc)[CT]
     }
   }
 
-  // Pass 2, channel tile outer: the tile's head, section (q, k, v), gains and
-  // rotation pair are fixed for all token rows.  GENERAL covers a wave with
-  // rows past the last one, channel tiles past the last head or v heads
-  // (by select, no divergent branch); every other wave takes the copy of the
-  // loop without those checks.
-  auto pass2 = [&](auto general) {
+  // Pass 2, channel tile outer, token tiles 2 HALF and 2 HALF + 1 into the slot:
+  // the tile's head, section (q, k, v), gains and rotation pair are fixed for
+  // all token rows.  GENERAL covers a wave with channel tiles past the last head
+  // or v heads (by select, no divergent branch); every other wave takes the copy
+  // of the loop without those checks.  Rows past the last one are computed from
+  // the repeated last row of x and never stored.
+  auto pass2 = [&](auto general, auto half_c) {
     constexpr bool GENERAL = decltype(general)::value;
+    constexpr int HALF = decltype(half_c)::value;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
       const int cl = ct * 16 + g4 * 4;
@@ -351,14 +470,13 @@ __device__ __forceinline__ void epilogue_qkv(const GemmArgs &a, f32x4 (&acc)[CT]
       const int which = gh / H;              // 0 q, 1 k, 2 v
       const int jd = cl - hh * D;            // dim within the head (multiple of 4)
       const bool norm = !GENERAL || which < 2;
-      float4 g = *reinterpret_cast<const float4 *>((which == 0 ? a.g_q : a.g_k) + jd);
+      float4 g = *reinterpret_cast<const float4 *>(gains + (which == 0 ? 0 : D) + jd);   // LDS copy of g_q | g_k
       if (which == 0) g = make_float4(g.x * a.q_scale, g.y * a.q_scale, g.z * a.q_scale, g.w * a.q_scale);
       const bool second = a.rope.kind == ST_ROPE_2D && jd >= D / 2;
       const int pair = (jd - (second ? D / 2 : 0)) >> 1;
-      u16 *dst = (which == 0 ? a.q : (which == 1 ? a.k : a.v)) + (gh - which * H) * D + jd;
 #pragma unroll
-      for (int tt = 0; tt < kTT; ++tt) {
-        if (GENERAL && roff[tt] < 0) continue;
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const int tt = HALF * 2 + t2;
         float invh = inv[tt][0];
 #pragma unroll
         for (int h2 = 1; h2 < HPW; ++h2) invh = hh == h2 ? inv[tt][h2] : invh;
@@ -379,13 +497,21 @@ __device__ __forceinline__ void epilogue_qkv(const GemmArgs &a, f32x4 (&acc)[CT]
         uint2 ov;
         ov.x = pack_bf16x2(o[0], o[1]);
         ov.y = pack_bf16x2(o[2], o[3]);
-        *reinterpret_cast<uint2 *>(dst + roff[tt]) = ov;
+        put(t2, ct, ov);
       }
     }
   };
-  const bool full_rows = m0 + kBM <= a.M;       // whole workgroup
-  if (full_rows && gh0 + HPW <= 2 * H) pass2(std::false_type{});   // q and k heads only, every row present
-  else pass2(std::true_type{});
+  if (gh0 + HPW <= 2 * H) {   // q and k heads only
+    pass2(std::false_type{}, H0{});
+    flush(H0{});
+    pass2(std::false_type{}, H1{});
+    flush(H1{});
+  } else {
+    pass2(std::true_type{}, H0{});
+    flush(H0{});
+    pass2(std::true_type{}, H1{});
+    flush(H1{});
+  }
 }
 
 template <int CT, int MODE, int D, bool XMAP = false>
@@ -422,6 +548,8 @@ st_status launch_qkv_bf16(const void *x, int64_t rows, int c_in, const void *w, 
   a.q_scale = q_scale;
   a.rope = rope;
   a.xmap = xmap;
+  // the epilogue stores 16-byte pieces of q, k, v rows
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v) & 15) return ST_EALIGN;
   const bool mapped = xmap.n1 != 0;
   switch (d) {
     case 72: return mapped ? launch_gemm<9, 1, 72, true>(a, s) : launch_gemm<9, 1, 72>(a, s);   // 2 heads x 72
