@@ -46,6 +46,9 @@ __device__ __forceinline__ void wait_vmem_upto() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
 
+// s_waitcnt lgkmcnt(0): this wave's LDS reads have returned.
+__device__ __forceinline__ void wait_lds_reads() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 struct GemmArgs {
   const u16 *x;      // [M, K]
   const u16 *w;      // [N, K]
@@ -148,28 +151,43 @@ struct GemmDma {
 };
 
 // One K step for one wave: issue the next step's loads into `nxt`, then
-// 2 x CT x 4 MFMAs on the stage in As / Bs.  Stage pointers are restrict-qualified:
-// the loads in flight never alias the stage being read.
+// 2 x CT x 4 MFMAs on the stage in As / Bs, in groups of one channel tile (4
+// MFMAs) whose A operand (and, at a K slice's first group, the 4 B operands)
+// is read from LDS one group ahead.  The wait at the top of a group is explicit
+// and comes before the next group's reads are issued: while direct-to-LDS
+// loads are in flight the compiler only ever waits for all outstanding LDS
+// reads, so a wait it placed after those reads would also wait for them.
+// Stage pointers are restrict-qualified: the loads in flight never alias the
+// stage being read.
 template <int CT, bool XMAP>
 __device__ __forceinline__ void gemm_step(const u16 *__restrict__ As, const u16 *__restrict__ Bs,
                                           u16 *__restrict__ nxt, bool prefetch, int k_next, const GemmDma<CT, XMAP> &dma,
                                           const u16 *xb, const u16 *w, int wave, int wn, int wm, int l16, int g4,
                                           f32x4 (&acc)[CT][kTT]) {
   typedef Tile<CT> TL;
+  constexpr int NG = (kBK / 32) * CT;   // groups (K slice ks, channel tile ct) of the step
   if (prefetch) dma.issue(nxt, k_next, xb, w, wave);
-#pragma unroll
-  for (int ks = 0; ks < kBK / 32; ++ks) {
-    bf16x8 bf[kTT];
-#pragma unroll
-    for (int tt = 0; tt < kTT; ++tt)
-      bf[tt] = *reinterpret_cast<const bf16x8 *>(Bs + slot_of(wm * kWM + tt * 16 + l16, ks * 4 + g4) * 8);
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      const bf16x8 af = *reinterpret_cast<const bf16x8 *>(As + slot_of(wn * TL::WN + ct * 16 + l16, ks * 4 + g4) * 8);
+  bf16x8 bfr[kBK / 32][kTT], afr[kBK / 32][CT];
+  auto issue_reads = [&](int gi) {
+    const int ks = gi / CT, ct = gi % CT;
+    if (ct == 0)
 #pragma unroll
       for (int tt = 0; tt < kTT; ++tt)
-        acc[ct][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[tt], acc[ct][tt], 0, 0, 0);
-    }
+        bfr[ks][tt] = *reinterpret_cast<const bf16x8 *>(Bs + slot_of(wm * kWM + tt * 16 + l16, ks * 4 + g4) * 8);
+    afr[ks][ct] = *reinterpret_cast<const bf16x8 *>(As + slot_of(wn * TL::WN + ct * 16 + l16, ks * 4 + g4) * 8);
+  };
+  issue_reads(0);
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    wait_lds_reads();
+    __builtin_amdgcn_sched_barrier(0);
+    if (gi + 1 < NG) issue_reads(gi + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    const int ks = gi / CT, ct = gi % CT;
+#pragma unroll
+    for (int tt = 0; tt < kTT; ++tt)
+      acc[ct][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[ks][ct], bfr[ks][tt], acc[ct][tt], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
