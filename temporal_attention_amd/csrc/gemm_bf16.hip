@@ -89,26 +89,30 @@ __device__ __forceinline__ int slot_of(int row, int kc) { return row * 8 + (kc ^
 
 // Epilogue staging.  A lane's accumulators hold 4 consecutive channels of one
 // token, so stores straight from them write 32-byte pieces of 16 different
-// rows per instruction.  Instead each wave converts half of its tile (32 tokens
-// x WN channels) to bf16 into its own LDS slot, reads it back along the rows and
+// rows per instruction.  Instead each wave converts ROWS tokens x WN channels
+// at a time to bf16 into its own LDS slot, reads them back along the rows and
 // stores 16 bytes per lane: a store instruction then covers whole stretches of
-// 3.5 token rows.  The slots reuse the pipeline stages, free after the K loop,
-// and need no workgroup barrier (a wave reads back only what it wrote).  Rows of
-// RS = 144 bf16 (288 bytes, 72 banks) put the 8-byte writes of 8 consecutive
-// rows x 4 lane groups on 64 distinct banks.
-template <int CT>
+// 3.5 token rows.  The slots sit in LDS the K loop no longer needs (ROWS = 32
+// when both stages are free, 16 when one already holds the next tile's first K
+// slice) and need no workgroup barrier (a wave reads back only what it wrote).
+// Rows of RS = 144 bf16 (288 bytes, 72 banks) put the 8-byte writes of 8
+// consecutive rows x 4 lane groups on 64 distinct banks.
+template <int CT, int ROWS>
 struct Staging {
   static constexpr int WN = 16 * CT;
   static constexpr int RS = WN == 128 ? 144 : WN;   // row stride in bf16
   static constexpr int CH = WN / 8;                 // 16-byte chunks per token row
-  static constexpr int SLOT = 32 * RS;              // bf16 per wave slot
+  static constexpr int SLOT = ROWS * RS;            // bf16 per wave slot
+  static constexpr int TPR = ROWS / 16;             // 16-token MFMA tiles per round
+  static constexpr int ROUNDS = kTT / TPR;
+  static constexpr int IT = (ROWS * CH + 63) / 64;  // 64-lane read-back steps per round
   static_assert(RS * 2 % 32 == 0 && (RS * 2 / 4) % 64 == 8, "row stride must spread 8 rows over the banks");
-  static_assert(CH % 2 == 0, "a half tile is whole 64-lane rounds");
+  static_assert(ROWS == 16 || ROWS == 32, "one or two token tiles per round");
 };
 
 // Global -> LDS loads of one stage: 1 KB (8 whole rows) per wavefront
-// instruction, lane l of block b filling slot 64 b + l.  Each lane's element offset inside the K
-// window is fixed for the whole K loop and computed once; rows past M or N
+// instruction, lane l of block b filling slot 64 b + l.  Each lane's element
+// offset inside a tile's K window is computed per tile; rows past M or N
 // repeat the last row (their results are never stored).  With XMAP the x rows
 // go through a.xmap and their offsets are from a.x (64-bit), else from the
 // tile's first row.
@@ -117,8 +121,11 @@ struct GemmDma {
   typedef Tile<CT> TL;
   typedef typename std::conditional<XMAP, int64_t, int>::type Off;
   Off off[TL::PER_WAVE];
+  const u16 *xb, *w;   // bases of the x offsets and of the W offsets
 
-  __device__ __forceinline__ void init(const GemmArgs &a, int64_t m0, int n0, int lane, int wave) {
+  __device__ __forceinline__ void set_tile(const GemmArgs &a, int64_t m0, int n0, int lane, int wave) {
+    xb = XMAP ? a.x : a.x + m0 * a.K;
+    w = a.w;
 #pragma unroll
     for (int i = 0; i < TL::PER_WAVE; ++i) {
       const int n = wave + TL::NWAVES * i;
@@ -135,38 +142,34 @@ struct GemmDma {
     }
   }
 
-  __device__ __forceinline__ void issue(u16 *__restrict__ stage, int k0, const u16 *xb, const u16 *w, int wave) const {
+  __device__ __forceinline__ void issue(u16 *__restrict__ stage, int k0, int wave) const {
 #pragma unroll
     for (int i = 0; i < TL::PER_WAVE; ++i) {
       const int n = wave + TL::NWAVES * i;
       if (n < TL::BLOCKS) {
         const bool isb = n >= TL::A_BLOCKS;
         const int b = isb ? n - TL::A_BLOCKS : n;
-        const u16 *src = (isb ? xb : w) + off[i] + k0;
-        u16 *dst = stage + (isb ? TL::LDS_A : 0) + b * 512;
-        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((isb ? xb : w) + off[i] + k0,
+                                         (__attribute__((address_space(3))) void *)(stage + (isb ? TL::LDS_A : 0) +
+                                                                                    b * 512),
+                                         16, 0, 0);
       }
     }
   }
 };
 
-// One K step for one wave: issue the next step's loads into `nxt`, then
-// 2 x CT x 4 MFMAs on the stage in As / Bs, in groups of one channel tile (4
-// MFMAs) whose A operand (and, at a K slice's first group, the 4 B operands)
-// is read from LDS one group ahead.  The wait at the top of a group is explicit
-// and comes before the next group's reads are issued: while direct-to-LDS
-// loads are in flight the compiler only ever waits for all outstanding LDS
-// reads, so a wait it placed after those reads would also wait for them.
-// Stage pointers are restrict-qualified: the loads in flight never alias the
-// stage being read.
-template <int CT, bool XMAP>
-__device__ __forceinline__ void gemm_step(const u16 *__restrict__ As, const u16 *__restrict__ Bs,
-                                          u16 *__restrict__ nxt, bool prefetch, int k_next, const GemmDma<CT, XMAP> &dma,
-                                          const u16 *xb, const u16 *w, int wave, int wn, int wm, int l16, int g4,
-                                          f32x4 (&acc)[CT][kTT]) {
+// The MFMAs of one K step for one wave: 2 x CT x 4 on the stage in As / Bs, in
+// groups of one channel tile (4 MFMAs) whose A operand (and, at a K slice's
+// first group, the 4 B operands) is read from LDS one group ahead.  The wait at
+// the top of a group is explicit and comes before the next group's reads are
+// issued: while direct-to-LDS loads are in flight the compiler only ever waits
+// for all outstanding LDS reads, so a wait it placed after those reads would
+// also wait for them.
+template <int CT>
+__device__ __forceinline__ void gemm_step(const u16 *__restrict__ As, const u16 *__restrict__ Bs, int wn, int wm,
+                                          int l16, int g4, f32x4 (&acc)[CT][kTT]) {
   typedef Tile<CT> TL;
   constexpr int NG = (kBK / 32) * CT;   // groups (K slice ks, channel tile ct) of the step
-  if (prefetch) dma.issue(nxt, k_next, xb, w, wave);
   bf16x8 bfr[kBK / 32][kTT], afr[kBK / 32][CT];
   auto issue_reads = [&](int gi) {
     const int ks = gi / CT, ct = gi % CT;
@@ -191,10 +194,6 @@ __device__ __forceinline__ void gemm_step(const u16 *__restrict__ As, const u16 
   }
 }
 
-template <int CT, int D, typename TabPtr>
-__device__ __forceinline__ void epilogue_qkv(const GemmArgs &a, f32x4 (&acc)[CT][kTT], int64_t m0, int nw0, int wm,
-                                             int lane, u16 *slot, const float *gains, TabPtr tab);
-
 // Orders a wave's LDS writes before its reads of other lanes' data (LDS executes
 // one wave's instructions in order; this only keeps the compiler from moving them).
 __device__ __forceinline__ void wave_lds_sync() {
@@ -210,115 +209,37 @@ __device__ __forceinline__ int64_t rope_table_floats(const RopeArgs &r) {
   return (int64_t)r.npos * (r.kind == ST_ROPE_2D ? D / 4 : D / 2) * 2;
 }
 
-// MODE 0: plain output y.  MODE 1: q/k/v with RMSNorm + RoPE on q, k (head dim D).
-template <int CT, int MODE, int D, bool XMAP>
-__global__ void __launch_bounds__(kThreads, 1) gemm_bf16_kernel(GemmArgs a, uint32_t n_tiles_n, uint32_t nblocks) {
-  typedef Tile<CT> TL;
-  __shared__ __attribute__((aligned(16))) u16 lds[kStages * TL::STAGE];
+// MODE 1: LDS past the two pipeline stages holds g_q | g_k (1 KB, fp32) and the
+// RoPE table when it fits, loaded once per workgroup; larger tables are read
+// from global memory.
+constexpr int kAuxU16 = 12288;    // 24 KB: 2 stages + aux stay within 160 KB
+constexpr int kGainsU16 = 512;
 
-  // Tile order: channel tiles in groups of kGroupN, token blocks running
-  // fastest inside a group, and each XCD taking a contiguous range of that
-  // order.  An XCD then streams activations past a ~2.6 MB slice of W that
-  // stays in its L2, instead of cycling through all of W per token block.
-  const uint32_t tile = xcd_remap(blockIdx.x, nblocks);
+// First token row and first channel of tile v: channel tiles in groups of
+// kGroupN, token blocks running fastest inside a group, and each XCD taking a
+// contiguous range of that order (xcd_remap), so an XCD streams activations
+// past a ~2.6 MB slice of W that stays in its L2.
+struct TileOrigin {
+  int64_t m0;
+  int n0;
+};
+template <int CT>
+__device__ __forceinline__ TileOrigin tile_origin(uint32_t v, uint32_t n_tiles_n, uint32_t nblocks) {
+  const uint32_t tile = xcd_remap(v, nblocks);
   const uint32_t n_tiles_m = nblocks / n_tiles_n;
   const uint32_t grp = tile / (kGroupN * n_tiles_m);
   const uint32_t gsz = min(kGroupN, n_tiles_n - grp * kGroupN);
   const uint32_t rem = tile - grp * kGroupN * n_tiles_m;
-  const int64_t m0 = (int64_t)(rem / gsz) * kBM;
-  const int n0 = (int)(grp * kGroupN + rem % gsz) * TL::BN;
+  return TileOrigin{(int64_t)(rem / gsz) * kBM, (int)(grp * kGroupN + rem % gsz) * Tile<CT>::BN};
+}
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int wn = wave & 1, wm = wave >> 1;   // 2 channel waves x kWavesM token waves
+// MODE 0 epilogue: the wave's 64 tokens x WN channels to y, through its slot.
+template <int CT, int ROWS>
+__device__ __forceinline__ void epilogue_plain(const GemmArgs &a, f32x4 (&acc)[CT][kTT], int64_t m0, int nw0,
+                                               int wm, int lane, u16 *slot) {
+  typedef Staging<CT, ROWS> SG;
   const int l16 = lane & 15, g4 = lane >> 4;
-
-  f32x4 acc[CT][kTT];
-#pragma unroll
-  for (int i = 0; i < CT; ++i)
-#pragma unroll
-    for (int j = 0; j < kTT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  GemmDma<CT, XMAP> dma;
-  dma.init(a, m0, n0, lane, wave);
-  const u16 *xb = XMAP ? a.x : a.x + m0 * a.K;
-  const int nk = a.K / kBK;
-  // MODE 1: the gains and the RoPE table move into the stage the last K step
-  // leaves free (their loads overlap that step's MFMAs): [gains 1 KB][table]
-  // [wave 7's staging slot].  The epilogue then issues no global loads once its
-  // stores have started (a load's wait would also wait for those stores).
-  // Tables too large for the stage are read from global memory.
-  constexpr int kGainsU16 = 512;   // 1 KB: g_q then g_k, fp32
-  int64_t tab_floats = 0;
-  if constexpr (MODE == 1) tab_floats = rope_table_floats<D>(a.rope);
-  const int64_t tab_u16 = (tab_floats * 2 + 127) & ~int64_t(127);
-  const bool tab_lds = tab_floats > 0 && kGainsU16 + tab_u16 + Staging<CT>::SLOT <= TL::STAGE;
-  dma.issue(lds, 0, xb, a.w, wave);
-  wait_vmem_upto<0>();
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    u16 *cur = lds + (kt & 1) * TL::STAGE;
-    u16 *nxt = lds + ((kt & 1) ^ 1) * TL::STAGE;
-    if constexpr (MODE == 1) {
-      if (kt + 1 == nk) {
-        static_assert(D <= 128, "g_q and g_k fill one 1 KB load");
-        if (wave == TL::NWAVES - 1) {   // lanes past 2 D re-read g_k's last 16 bytes into the gains block's tail
-          const float *g = lane < D / 4 ? a.g_q + 4 * lane : a.g_k + 4 * min(lane - D / 4, D / 4 - 1);
-          __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)nxt, 16, 0, 0);
-        }
-        if (tab_lds) {
-          // 1 KB per wave instruction; the last block's lanes past the end re-read the last 16 bytes
-          const int blocks = (int)((tab_floats + 255) / 256);
-          for (int b = wave; b < blocks; b += TL::NWAVES) {
-            const int64_t f = min<int64_t>((int64_t)b * 256 + lane * 4, tab_floats - 4);
-            __builtin_amdgcn_global_load_lds(a.rope.table + f,
-                                             (__attribute__((address_space(3))) void *)(nxt + kGainsU16 + b * 512), 16,
-                                             0, 0);
-          }
-        }
-      }
-    }
-    gemm_step<CT, XMAP>(cur, cur + TL::LDS_A, nxt, kt + 1 < nk, (kt + 1) * kBK, dma, xb, a.w, wave, wn, wm, l16, g4,
-                        acc);
-    wait_vmem_upto<0>();
-    __syncthreads();
-  }
-
-  // ------------------------------------------------------------------ epilogue
-  typedef Staging<CT> SG;
-  const int nw0 = n0 + wn * TL::WN;   // first channel of this wave
-  if constexpr (MODE == 0) {
-    if (a.N % 8 == 0 && (reinterpret_cast<uintptr_t>(a.y) & 15) == 0) {
-      static_assert(8 * SG::SLOT <= kStages * TL::STAGE, "wave slots fit the stages");
-      u16 *slot = lds + wave * SG::SLOT;
-      const int64_t rl = m0 + wm * kWM + lane;   // the lane's token row, mapped once
-      const int64_t roff = rl < a.M ? map_row(rl, a.ymap) * a.N : -1;
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-          for (int ct = 0; ct < CT; ++ct) {
-            const f32x4 &c = acc[ct][half * 2 + t2];
-            uint2 o;
-            o.x = pack_bf16x2(c[0], c[1]);
-            o.y = pack_bf16x2(c[2], c[3]);
-            *reinterpret_cast<uint2 *>(slot + (t2 * 16 + l16) * SG::RS + ct * 16 + g4 * 4) = o;
-          }
-        wave_lds_sync();
-#pragma unroll
-        for (int it = 0; it < SG::CH / 2; ++it) {
-          const int c = it * 64 + lane;
-          const int tok = c / SG::CH, ch = c - tok * SG::CH;
-          const int64_t ro = __shfl(roff, half * 32 + tok);
-          const uint4 v = *reinterpret_cast<const uint4 *>(slot + tok * SG::RS + ch * 8);
-          const int n = nw0 + ch * 8;
-          if (ro >= 0 && n < a.N) *reinterpret_cast<uint4 *>(a.y + ro + n) = v;
-        }
-        wave_lds_sync();
-      }
-      return;
-    }
+  if (a.N % 8 != 0 || (reinterpret_cast<uintptr_t>(a.y) & 15) != 0) {   // rows not 16-byte aligned: direct
 #pragma unroll
     for (int tt = 0; tt < kTT; ++tt) {
       const int64_t r = m0 + wm * kWM + tt * 16 + l16;
@@ -328,35 +249,45 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_bf16_kernel(GemmArgs a, uint
       for (int ct = 0; ct < CT; ++ct) {
         const int n = nw0 + ct * 16 + g4 * 4;
         if (n >= a.N) continue;
-        uint2 o;
-        o.x = pack_bf16x2(acc[ct][tt][0], acc[ct][tt][1]);
-        o.y = pack_bf16x2(acc[ct][tt][2], acc[ct][tt][3]);
-        *reinterpret_cast<uint2 *>(yr + n) = o;
+        *reinterpret_cast<uint2 *>(yr + n) =
+            uint2{pack_bf16x2(acc[ct][tt][0], acc[ct][tt][1]), pack_bf16x2(acc[ct][tt][2], acc[ct][tt][3])};
       }
     }
-  } else {
-    // Wave slots: waves 0-6 in the other stage, wave 7 after the gains and table.
-    static_assert(7 * SG::SLOT <= TL::STAGE, "seven wave slots fit one stage");
-    static_assert(kGainsU16 + SG::SLOT <= TL::STAGE, "gains and one slot fit one stage");
-    u16 *tstage = lds + (nk & 1) * TL::STAGE;
-    u16 *slot = wave < 7 ? lds + ((nk & 1) ^ 1) * TL::STAGE + wave * SG::SLOT
-                         : tstage + kGainsU16 + (tab_lds ? tab_u16 : 0);
-    const float *gl = reinterpret_cast<const float *>(tstage);
-    if (tab_lds) {
-      epilogue_qkv<CT, D>(a, acc, m0, nw0, wm, lane, slot, gl, reinterpret_cast<const float *>(tstage + kGainsU16));
-    } else {
-      epilogue_qkv<CT, D>(a, acc, m0, nw0, wm, lane, slot, gl, a.rope.table);
+    return;
+  }
+  const int64_t rl = m0 + wm * kWM + lane;   // the lane's token row, mapped once
+  const int64_t roff = rl < a.M ? map_row(rl, a.ymap) * a.N : -1;
+#pragma unroll
+  for (int rd = 0; rd < SG::ROUNDS; ++rd) {
+#pragma unroll
+    for (int t2 = 0; t2 < SG::TPR; ++t2)
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const f32x4 &c = acc[ct][rd * SG::TPR + t2];
+        *reinterpret_cast<uint2 *>(slot + (t2 * 16 + l16) * SG::RS + ct * 16 + g4 * 4) =
+            uint2{pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3])};
+      }
+    wave_lds_sync();
+#pragma unroll
+    for (int it = 0; it < SG::IT; ++it) {
+      const int c = min(it * 64 + lane, ROWS * SG::CH - 1);
+      const int tok = c / SG::CH, ch = c - tok * SG::CH;
+      const int64_t ro = __shfl(roff, rd * ROWS + tok);
+      const uint4 v = *reinterpret_cast<const uint4 *>(slot + tok * SG::RS + ch * 8);
+      const int n = nw0 + ch * 8;
+      if (it * 64 + lane < ROWS * SG::CH && ro >= 0 && n < a.N) *reinterpret_cast<uint4 *>(a.y + ro + n) = v;
     }
+    wave_lds_sync();
   }
 }
 
 // MODE 1 epilogue: the wave's channels are HPW whole heads; the results go out
-// through the wave's slot (Staging), half a tile at a time.
-template <int CT, int D, typename TabPtr>
+// through the wave's slot, ROWS tokens at a time.
+template <int CT, int D, int ROWS, typename TabPtr>
 __device__ __forceinline__ void epilogue_qkv(const GemmArgs &a, f32x4 (&acc)[CT][kTT], int64_t m0, int nw0, int wm,
                                              int lane, u16 *slot, const float *gains, TabPtr tab) {
   typedef Tile<CT> TL;
-  typedef Staging<CT> SG;
+  typedef Staging<CT, ROWS> SG;
   constexpr int HPW = TL::WN / D;
   static_assert(TL::WN % D == 0, "wave channel range must hold whole heads");
   static_assert(D % 8 == 0, "a 16-byte chunk must not straddle two heads");
@@ -375,17 +306,17 @@ __device__ __forceinline__ void epilogue_qkv(const GemmArgs &a, f32x4 (&acc)[CT]
     hok[hh] = gh < 3 * H;
     hbase[hh] = (which == 0 ? a.q : (which == 1 ? a.k : a.v)) + (gh - which * H) * D;
   }
-  // Stores half `half` of the wave's tile from its slot: chunk c of the half is
-  // 8 channels of token row c / CH, inside one head.
-  auto flush = [&](auto half_c) {
-    constexpr int half = decltype(half_c)::value;
+  // Stores round RD of the wave from its slot: chunk c is 8 channels of token
+  // row c / CH of the round, inside one head.
+  auto flush = [&](auto rd_c) {
+    constexpr int RD = decltype(rd_c)::value;
     wave_lds_sync();
 #pragma unroll
-    for (int it = 0; it < SG::CH / 2; ++it) {
-      const int c = it * 64 + lane;
+    for (int it = 0; it < SG::IT; ++it) {
+      const int c = min(it * 64 + lane, ROWS * SG::CH - 1);
       const int tok = c / SG::CH, ch = c - tok * SG::CH;
       const int cl = ch * 8, hh = cl / D;
-      const int64_t r = m0 + wm * kWM + half * 32 + tok;
+      const int64_t r = m0 + wm * kWM + RD * ROWS + tok;
       const uint4 v = *reinterpret_cast<const uint4 *>(slot + tok * SG::RS + cl);
       u16 *base = hbase[0];
       bool ok = hok[0];
@@ -394,32 +325,42 @@ __device__ __forceinline__ void epilogue_qkv(const GemmArgs &a, f32x4 (&acc)[CT]
         base = hh == h2 ? hbase[h2] : base;
         ok = hh == h2 ? hok[h2] : ok;
       }
-      if (r < a.M && ok) *reinterpret_cast<uint4 *>(base + r * hd + (cl - hh * D)) = v;
+      if (it * 64 + lane < ROWS * SG::CH && r < a.M && ok)
+        *reinterpret_cast<uint4 *>(base + r * hd + (cl - hh * D)) = v;
     }
     wave_lds_sync();
   };
   auto put = [&](int t2, int ct, const uint2 &o) {
     *reinterpret_cast<uint2 *>(slot + (t2 * 16 + l16) * SG::RS + ct * 16 + g4 * 4) = o;
   };
+  typedef std::integral_constant<int, 0> T0;
+  typedef std::integral_constant<int, 1> T1;
+  typedef std::integral_constant<int, 2> T2;
+  typedef std::integral_constant<int, 3> T3;
 
-  typedef std::integral_constant<int, 0> H0;
-  typedef std::integral_constant<int, 1> H1;
+  // Every round of the wave's tile, in order.
+  auto rounds = [&](auto fn) {
+    fn(T0{});
+    fn(T1{});
+    if constexpr (SG::ROUNDS == 4) {
+      fn(T2{});
+      fn(T3{});
+    }
+  };
 
   // A wave whose heads are all v heads stores the projection as it is.
   if (gh0 / H == 2 && (gh0 + HPW - 1) / H == 2) {
-    auto half_v = [&](auto half_c) {
-      constexpr int half = decltype(half_c)::value;
+    rounds([&](auto rd_c) {
+      constexpr int RD = decltype(rd_c)::value;
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2)
+      for (int t2 = 0; t2 < SG::TPR; ++t2)
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
-          const f32x4 &c = acc[ct][half * 2 + t2];
+          const f32x4 &c = acc[ct][RD * SG::TPR + t2];
           put(t2, ct, uint2{pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3])});
         }
-      flush(half_c);
-    };
-    half_v(H0{});
-    half_v(H1{});
+      flush(rd_c);
+    });
     return;
   }
 
@@ -430,7 +371,7 @@ __device__ __forceinline__ void epilogue_qkv(const GemmArgs &a, f32x4 (&acc)[CT]
   float inv[kTT][HPW];
   int p0[kTT], p1[kTT];
   const uint32_t period = (uint32_t)min<int64_t>(a.rope.period, 1ll << 30);
-  const uint32_t base_i = a.rope.kind == ST_ROPE_NONE ? 0u : (uint32_t)(m0 % a.rope.period);   // one per workgroup
+  const uint32_t base_i = a.rope.kind == ST_ROPE_NONE ? 0u : (uint32_t)(m0 % a.rope.period);   // one per tile
 #pragma unroll
   for (int tt = 0; tt < kTT; ++tt) {
     float ss[HPW];
@@ -470,15 +411,15 @@ __device__ __forceinline__ void epilogue_qkv(const GemmArgs &a, f32x4 (&acc)[CT]
     }
   }
 
-  // Pass 2, channel tile outer, token tiles 2 HALF and 2 HALF + 1 into the slot:
-  // the tile's head, section (q, k, v), gains and rotation pair are fixed for
-  // all token rows.  GENERAL covers a wave with channel tiles past the last head
-  // or v heads (by select, no divergent branch); every other wave takes the copy
-  // of the loop without those checks.  Rows past the last one are computed from
-  // the repeated last row of x and never stored.
-  auto pass2 = [&](auto general, auto half_c) {
+  // Pass 2, round RD, channel tile outer, into the slot: the tile's head,
+  // section (q, k, v), gains and rotation pair are fixed for all token rows.
+  // GENERAL covers a wave with channel tiles past the last head or v heads (by
+  // select, no divergent branch); every other wave takes the copy of the loop
+  // without those checks.  Rows past the last one are computed from the
+  // repeated (or zero) last rows of x and never stored.
+  auto pass2 = [&](auto general, auto rd_c) {
     constexpr bool GENERAL = decltype(general)::value;
-    constexpr int HALF = decltype(half_c)::value;
+    constexpr int RD = decltype(rd_c)::value;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
       const int cl = ct * 16 + g4 * 4;
@@ -493,13 +434,13 @@ __device__ __forceinline__ void epilogue_qkv(const GemmArgs &a, f32x4 (&acc)[CT]
       const bool second = a.rope.kind == ST_ROPE_2D && jd >= D / 2;
       const int pair = (jd - (second ? D / 2 : 0)) >> 1;
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        const int tt = HALF * 2 + t2;
+      for (int t2 = 0; t2 < SG::TPR; ++t2) {
+        const int tt = RD * SG::TPR + t2;
         float invh = inv[tt][0];
 #pragma unroll
         for (int h2 = 1; h2 < HPW; ++h2) invh = hh == h2 ? inv[tt][h2] : invh;
-        float o[4] = {acc[ct][tt][0] * invh * g.x, acc[ct][tt][1] * invh * g.y, acc[ct][tt][2] * invh * g.z,
-                      acc[ct][tt][3] * invh * g.w};
+        const f32x4 &c = acc[ct][tt];
+        float o[4] = {c[0] * invh * g.x, c[1] * invh * g.y, c[2] * invh * g.z, c[3] * invh * g.w};
         if (a.rope.kind != ST_ROPE_NONE) {
           const int pos = second ? p1[tt] : p0[tt];
           const float4 cs = *reinterpret_cast<const float4 *>(tab + ((int64_t)pos * npairs + pair) * 2);
@@ -511,25 +452,152 @@ __device__ __forceinline__ void epilogue_qkv(const GemmArgs &a, f32x4 (&acc)[CT]
         }
         if (GENERAL)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) o[j] = norm ? o[j] : acc[ct][tt][j];
-        uint2 ov;
-        ov.x = pack_bf16x2(o[0], o[1]);
-        ov.y = pack_bf16x2(o[2], o[3]);
-        put(t2, ct, ov);
+          for (int j = 0; j < 4; ++j) o[j] = norm ? o[j] : c[j];
+        put(t2, ct, uint2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])});
       }
     }
+    flush(rd_c);
   };
-  if (gh0 + HPW <= 2 * H) {   // q and k heads only
-    pass2(std::false_type{}, H0{});
-    flush(H0{});
-    pass2(std::false_type{}, H1{});
-    flush(H1{});
-  } else {
-    pass2(std::true_type{}, H0{});
-    flush(H0{});
-    pass2(std::true_type{}, H1{});
-    flush(H1{});
+  if (gh0 + HPW <= 2 * H) rounds([&](auto rd_c) { pass2(std::false_type{}, rd_c); });   // q and k heads only
+  else rounds([&](auto rd_c) { pass2(std::true_type{}, rd_c); });
+}
+
+// MODE 0: plain output y.  MODE 1: q/k/v with RMSNorm + RoPE on q, k (head dim D).
+// PERSIST (MODE 0 without XMAP): workgroup b takes tiles b, b + gridDim.x, ...
+// (tile_origin order), and the K pipeline runs on across tiles: the last K
+// step of a tile loads the next tile's first K slice into the free stage, and
+// the next tile's second slice is issued right after the epilogue, so one
+// tile's stores drain while the next one computes, and no workgroup waits for
+// its stores to retire before the next tile's loads start.  The other kernels
+// take one tile per workgroup (their longer epilogues need more registers
+// than the tile loop leaves).
+template <int CT, int MODE, int D, bool XMAP>
+__global__ void __launch_bounds__(kThreads, 1) gemm_bf16_kernel(GemmArgs a, uint32_t n_tiles_n, uint32_t nblocks) {
+  typedef Tile<CT> TL;
+  constexpr bool PERSIST = MODE == 0 && !XMAP;
+  constexpr int ROWS = PERSIST ? 16 : 32;   // staging rows per round: one stage free, or both
+  typedef Staging<CT, ROWS> SG;
+  static_assert(8 * SG::SLOT <= (PERSIST ? 1 : kStages) * TL::STAGE, "the wave slots fit the free stages");
+  __shared__ __attribute__((aligned(16))) u16 lds[kStages * TL::STAGE + (MODE == 1 ? kAuxU16 : 0)];
+  typedef __attribute__((address_space(3))) void lds_void;
+
+  uint32_t v = blockIdx.x;
+  if (v >= nblocks) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = PERSIST ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : threadIdx.x >> 6;
+  const int wn = wave & 1, wm = wave >> 1;   // 2 channel waves x kWavesM token waves
+  const int nk = a.K / kBK;
+
+  u16 *aux = lds + kStages * TL::STAGE;
+  bool tab_lds = false;
+  if constexpr (MODE == 1) {
+    static_assert(D <= 128, "g_q and g_k fill one 1 KB load");
+    const int64_t tab_floats = rope_table_floats<D>(a.rope);
+    const int blocks = (int)((tab_floats + 255) / 256);   // 1 KB per wave instruction
+    tab_lds = tab_floats > 0 && kGainsU16 + blocks * 512 <= kAuxU16;
+    if (wave == TL::NWAVES - 1) {   // lanes past 2 D re-read g_k's last 16 bytes into the gains block's tail
+      const float *g = lane < D / 4 ? a.g_q + 4 * lane : a.g_k + 4 * min(lane - D / 4, D / 4 - 1);
+      __builtin_amdgcn_global_load_lds(g, (lds_void *)aux, 16, 0, 0);
+    }
+    if (tab_lds)   // the last block's lanes past the end re-read the last 16 bytes
+      for (int b = wave; b < blocks; b += TL::NWAVES) {
+        const int64_t f = min<int64_t>((int64_t)b * 256 + lane * 4, tab_floats - 4);
+        __builtin_amdgcn_global_load_lds(a.rope.table + f, (lds_void *)(aux + kGainsU16 + b * 512), 16, 0, 0);
+      }
   }
+
+  TileOrigin o = tile_origin<CT>(v, n_tiles_n, nblocks);
+  GemmDma<CT, XMAP> dma;
+  dma.set_tile(a, o.m0, o.n0, lane, wave);
+  dma.issue(lds, 0, wave);
+  wait_vmem_upto<0>();
+  __syncthreads();
+
+  int st = 0;                   // stage holding the current K slice
+  bool second_loaded = false;   // the tile's second K slice was issued before its first step
+  f32x4 acc[CT][kTT];
+  while (true) {
+    const uint32_t vn = v + gridDim.x;
+    const bool has_next = PERSIST && vn < nblocks;
+    // The lane index, opaque to the compiler once per tile: keeps it from
+    // hoisting the epilogue's per-lane address arithmetic out of the tile loop
+    // and holding dozens of such values live across the K loop.
+    int ln = lane;
+#if defined(__HIP_DEVICE_COMPILE__)
+    if constexpr (PERSIST) asm volatile("" : "+v"(ln));
+#endif
+    const int l16 = ln & 15, g4 = ln >> 4;
+    TileOrigin on = o;
+#pragma unroll
+    for (int i = 0; i < CT; ++i)
+#pragma unroll
+      for (int j = 0; j < kTT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kt = 0; kt + 1 < nk; ++kt) {
+      u16 *cur = lds + st * TL::STAGE;
+      if (kt > 0 || !second_loaded) dma.issue(lds + (st ^ 1) * TL::STAGE, (kt + 1) * kBK, wave);
+      gemm_step<CT>(cur, cur + TL::LDS_A, wn, wm, l16, g4, acc);
+      wait_vmem_upto<0>();
+      __syncthreads();
+      st ^= 1;
+    }
+    {   // the last K step loads the next tile's first K slice
+      u16 *cur = lds + st * TL::STAGE;
+      if (has_next) {
+        on = tile_origin<CT>(vn, n_tiles_n, nblocks);
+        dma.set_tile(a, on.m0, on.n0, ln, wave);   // ln: recomputed per tile, not hoisted
+        dma.issue(lds + (st ^ 1) * TL::STAGE, 0, wave);
+      }
+      gemm_step<CT>(cur, cur + TL::LDS_A, wn, wm, l16, g4, acc);
+      wait_vmem_upto<0>();
+      __syncthreads();
+      st ^= 1;
+    }
+
+    // Epilogue: PERSIST, in the stage the last step has left free (st ^ 1;
+    // stage st holds the next tile's first K slice); otherwise in both stages.
+    u16 *slot = (PERSIST ? lds + (st ^ 1) * TL::STAGE : lds) + wave * SG::SLOT;
+    const int nw0 = o.n0 + wn * TL::WN;   // first channel of this wave
+    if constexpr (MODE == 0) {
+      epilogue_plain<CT, ROWS>(a, acc, o.m0, nw0, wm, ln, slot);
+    } else {
+      const float *gl = reinterpret_cast<const float *>(aux);
+      if (tab_lds)
+        epilogue_qkv<CT, D, ROWS>(a, acc, o.m0, nw0, wm, ln, slot, gl,
+                                  reinterpret_cast<const float *>(aux + kGainsU16));
+      else
+        epilogue_qkv<CT, D, ROWS>(a, acc, o.m0, nw0, wm, ln, slot, gl, a.rope.table);
+    }
+    if (!has_next) break;
+    __syncthreads();   // every wave has read back its slot: the stage takes the next tile's second K slice
+    second_loaded = nk > 1;
+    if (second_loaded) dma.issue(lds + (st ^ 1) * TL::STAGE, kBK, wave);
+    v = vn;
+    o = on;
+  }
+}
+
+// Every kernel the launchers below use, instantiated explicitly so that the
+// host pass emits all of their launch stubs.
+template __global__ void gemm_bf16_kernel<9, 1, 72, false>(GemmArgs, uint32_t, uint32_t);
+template __global__ void gemm_bf16_kernel<9, 1, 72, true>(GemmArgs, uint32_t, uint32_t);
+template __global__ void gemm_bf16_kernel<8, 1, 64, false>(GemmArgs, uint32_t, uint32_t);
+template __global__ void gemm_bf16_kernel<8, 1, 64, true>(GemmArgs, uint32_t, uint32_t);
+template __global__ void gemm_bf16_kernel<8, 1, 128, false>(GemmArgs, uint32_t, uint32_t);
+template __global__ void gemm_bf16_kernel<8, 1, 128, true>(GemmArgs, uint32_t, uint32_t);
+template __global__ void gemm_bf16_kernel<9, 0, 0, false>(GemmArgs, uint32_t, uint32_t);
+template __global__ void gemm_bf16_kernel<8, 0, 0, false>(GemmArgs, uint32_t, uint32_t);
+
+// Compute units of the current device (cached per device): the persistent grid.
+int device_cus() {
+  static int cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
 }
 
 template <int CT, int MODE, int D, bool XMAP = false>
@@ -540,8 +608,10 @@ st_status launch_gemm(const GemmArgs &a, hipStream_t s) {
   const uint32_t nt = (a.N + TL::BN - 1) / TL::BN;
   const int64_t nb = mt * nt;
   if (nb >= (1ll << 31)) return ST_EUNSUPPORTED;
-  hipLaunchKernelGGL((gemm_bf16_kernel<CT, MODE, D, XMAP>), dim3((uint32_t)nb), dim3(kThreads), 0, s, a, nt,
-                     (uint32_t)nb);
+  // persistent: one workgroup per CU (LDS-bound); otherwise one tile per workgroup
+  const bool persist = MODE == 0 && !XMAP;
+  const uint32_t grid = persist ? (uint32_t)std::min<int64_t>(nb, device_cus()) : (uint32_t)nb;
+  hipLaunchKernelGGL((gemm_bf16_kernel<CT, MODE, D, XMAP>), dim3(grid), dim3(kThreads), 0, s, a, nt, (uint32_t)nb);
   return launch_status();
 }
 
