@@ -555,7 +555,7 @@ def main():
         "timing": "per-kernel figures are medians over the timed steps of HIP events on the launch stream",
         "kernels": kernels,
         "qkv_epilogue": epilogue,
-        "roofline": {"kernel": "attn_long_kernel<72,2> (spatial attention)", "bound": "mfma",
+        "roofline": {"kernel": "attn_long_kernel<72, 2, true> (spatial attention)", "bound": "mfma",
                      "achieved": round(attn_achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": None if traffic is None else round(traffic / 1e9, 4),

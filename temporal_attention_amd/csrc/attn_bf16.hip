@@ -410,12 +410,18 @@ struct LongWave {
   __device__ __forceinline__ void step(f32x16 (&sb)[2][NT], bf16x8 (&kf)[DM::KS], const u16 *__restrict__ Vs, int un,
                                        bool mask_next, const u16 *__restrict__ Kp, int up) {
     bf16x8 pf[2][NT];
+    // Raised issue priority while this wave interleaves S^T MFMAs with
+    // exponentials: when the other wave of the SIMD is in its P.V phase
+    // (MFMA-heavy, waiting on V^T reads), this one's vector work goes first
+    // and fills the matrix pipe's shadow.
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       if constexpr (NEXT) qk(sb[CUR ^ 1][nt], kf, nt);
       probs(sb[CUR][nt], pf, nt);
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
     pv(pf, Vs);
     if constexpr (PREF) kfrag(kf, Kp, up);
     if constexpr (NEXT) {

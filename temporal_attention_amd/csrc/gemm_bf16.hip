@@ -37,7 +37,7 @@ constexpr int kWavesM = 4;        // token-direction waves per workgroup
 constexpr int kThreads = 64 * 2 * kWavesM;
 constexpr int kBM = kWavesM * kWM;  // tokens per workgroup
 constexpr int kStages = 2;       // LDS pipeline depth
-constexpr uint32_t kGroupN = 16; // channel tiles sharing a token-block sweep
+constexpr uint32_t kGroupN = 16; // channel tiles per group of the tile order (tile_origin)
 
 // s_waitcnt vmcnt(N): at most N of this wave's vector-memory operations outstanding.
 template <int N>
@@ -215,10 +215,14 @@ __device__ __forceinline__ int64_t rope_table_floats(const RopeArgs &r) {
 constexpr int kAuxU16 = 12288;    // 24 KB: 2 stages + aux stay within 160 KB
 constexpr int kGainsU16 = 512;
 
-// First token row and first channel of tile v: channel tiles in groups of
-// kGroupN, token blocks running fastest inside a group, and each XCD taking a
-// contiguous range of that order (xcd_remap), so an XCD streams activations
-// past a ~2.6 MB slice of W that stays in its L2.
+// First token row and first channel of tile v.  Channel tiles go in groups of
+// kGroupN; inside a group the channel tiles of one token block run back to
+// back (they share the block's activations in the XCD's L2), then the next
+// token block; each XCD takes a contiguous range of that order (xcd_remap).
+// A 1152-wide projection (4 channel tiles, 2.6 MB of W) keeps its weights in
+// L2; the 3456-wide QKV weights (8 MB) are re-read from the Infinity Cache per
+// token block, which measured faster than orders that keep a 4-tile weight
+// slice in L2 and re-read activations instead.
 struct TileOrigin {
   int64_t m0;
   int n0;
