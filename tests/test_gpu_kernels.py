@@ -218,8 +218,12 @@ def test_qkv_zero_rows_is_noop():
 # --------------------------------------------------------------------------- #
 # Output projection                                                            #
 # --------------------------------------------------------------------------- #
+# The bf16 projection runs one workgroup per CU over its tiles once there are more tiles than
+# CUs: 51,277 ragged rows (804 tiles, ~3 per workgroup), a single K step per tile (K = 64,
+# 300 tiles), and 100 outputs (rows not 16-byte aligned: the 8-byte store path, 274 tiles).
 @pytest.mark.parametrize("rows,K,N,dt", [(300, 1152, 1152, BF), (129, 384, 384, BF), (50, 1152, 100, BF),
-                                         (64, 128, 128, F32)])
+                                         (64, 128, 128, F32), (51277, 1152, 1152, BF), (76800, 64, 288, BF),
+                                         (70000, 1152, 100, BF)])
 def test_out_proj(rows, K, N, dt):
     sd = "bf16" if dt == BF else "f32"
     a = st_synth.randn((rows, K), 21 + rows, dtype=sd)
@@ -234,7 +238,7 @@ def test_out_proj(rows, K, N, dt):
 # multiple of 256), the 288-channel and the 256-channel tilings, fp32
 @pytest.mark.parametrize("outer,n1,n2,K,N,dt", [(2, 5, 37, 1152, 1152, BF), (1, 51, 13, 384, 384, BF),
                                                 (3, 7, 9, 1152, 100, BF), (1, 4, 6, 128, 128, F32),
-                                                (1, 1, 70, 128, 64, BF)])
+                                                (1, 1, 70, 128, 64, BF), (1, 51, 1020, 1152, 1152, BF)])
 def test_out_proj_relayout(outer, n1, n2, K, N, dt):
     sd = "bf16" if dt == BF else "f32"
     rows = outer * n1 * n2
