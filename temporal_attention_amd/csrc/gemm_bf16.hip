@@ -23,6 +23,7 @@
 // as large as the LDS allows and every load instruction covers whole lines.
 // The grid is remapped so the channel tiles of one token block run on the same
 // XCD and share its L2 copy of the activations.
+#include <atomic>
 #include <type_traits>
 
 #include "st_internal.h"
@@ -591,17 +592,18 @@ template __global__ void gemm_bf16_kernel<8, 1, 128, true>(GemmArgs, uint32_t, u
 template __global__ void gemm_bf16_kernel<9, 0, 0, false>(GemmArgs, uint32_t, uint32_t);
 template __global__ void gemm_bf16_kernel<8, 0, 0, false>(GemmArgs, uint32_t, uint32_t);
 
-// Compute units of the current device (cached per device): the persistent grid.
+// Compute units of the current device (cached per device; concurrent first
+// calls store the same value): the persistent grid.
 int device_cus() {
-  static int cache[64] = {};
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int n = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
-    cache[dev] = n;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return n;
 }
 
 template <int CT, int MODE, int D, bool XMAP = false>
