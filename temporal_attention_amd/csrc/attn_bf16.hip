@@ -31,7 +31,8 @@
 // global -> LDS into a private slice, read back as V^T by transpose reads; a
 // workgroup covers four adjacent heads of one outer index, so its loads share
 // cache lines, and every wave has exactly one head to do, so all of them are
-// in flight at once.
+// in flight at once.  For d = 72 the output rows go back out through the same
+// slice, 16 bytes per lane along whole rows.
 #include <math.h>
 
 #include "st_internal.h"
@@ -836,36 +837,49 @@ attn_short_kernel(AttnArgs a, uint32_t nblocks) {
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
+    if constexpr (D % 64 != 0) {
+      // d = 72 (rows of 144 bytes, 36 banks apart): O^T of both query tiles, then
+      // the normalised rows through this wave's V slice (free once the last P.V
+      // MFMA has read it), stored 16 bytes per lane along whole rows instead of
+      // 8-byte pieces of 32 rows.  For d = 64 or 128 the rows would all start on
+      // the same LDS banks; those store from the accumulators directly.
+      f32x16 oacc[NT][DM::DT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      f32x16 oacc[DM::DT];
+      for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
-      for (int dt = 0; dt < DM::DT; ++dt)
+        for (int dt = 0; dt < DM::DT; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
+          for (int r = 0; r < 16; ++r) oacc[nt][dt][r] = 0.f;
 #pragma unroll
-      for (int mt = 0; mt < NT; ++mt)
+        for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
-        for (int ks2 = 0; ks2 < 2; ++ks2) {
-          const u16 *vb = Vs + (mt * 32 + ks2 * 16) * D + v_off;
+          for (int ks2 = 0; ks2 < 2; ++ks2) {
+            const u16 *vb = Vs + (mt * 32 + ks2 * 16) * D + v_off;
 #pragma unroll
-          for (int dt = 0; dt < DM::DT; ++dt) {
-            uint4 u = tr_read_pair<D>(vb + dt * 32);
-            if (DM::DV != D && dt == DM::DT - 1 && !vkeep) u = make_uint4(vconst, vconst, vconst, vconst);
-            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u), pf[nt][mt][ks2], oacc[dt],
-                                                               0, 0, 0);
+            for (int dt = 0; dt < DM::DT; ++dt) {
+              uint4 u = tr_read_pair<D>(vb + dt * 32);
+              if (DM::DV != D && dt == DM::DT - 1 && !vkeep) u = make_uint4(vconst, vconst, vconst, vconst);
+              oacc[nt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u), pf[nt][mt][ks2],
+                                                                     oacc[nt][dt], 0, 0, 0);
+            }
           }
-        }
-      float l;
-      if constexpr (DM::ONES) {
-        l = __shfl(oacc[DM::ONES_DT][DM::ONES_R], l32);
-      } else {
-        l = lsum[nt];
       }
-      const float inv = 1.0f / l;
-      const int qi = nt * 32 + l32;
-      if (qi < L) {
-        u16 *orow = op + (int64_t)qi * rs;
+      float inv[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        float l;
+        if constexpr (DM::ONES) {
+          l = __shfl(oacc[nt][DM::ONES_DT][DM::ONES_R], l32);
+        } else {
+          l = lsum[nt];
+        }
+        inv[nt] = 1.0f / l;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int dt = 0; dt < DM::DT; ++dt)
 #pragma unroll
@@ -873,11 +887,69 @@ attn_short_kernel(AttnArgs a, uint32_t nblocks) {
             const int dd = dt * 32 + rb * 8 + g * 4;
             if (dd + 4 <= D) {
               uint2 w;
-              w.x = pack_bf16x2(oacc[dt][rb * 4 + 0] * inv, oacc[dt][rb * 4 + 1] * inv);
-              w.y = pack_bf16x2(oacc[dt][rb * 4 + 2] * inv, oacc[dt][rb * 4 + 3] * inv);
-              *reinterpret_cast<uint2 *>(orow + dd) = w;
+              w.x = pack_bf16x2(oacc[nt][dt][rb * 4 + 0] * inv[nt], oacc[nt][dt][rb * 4 + 1] * inv[nt]);
+              w.y = pack_bf16x2(oacc[nt][dt][rb * 4 + 2] * inv[nt], oacc[nt][dt][rb * 4 + 3] * inv[nt]);
+              *reinterpret_cast<uint2 *>(Vs + (nt * 32 + l32) * D + dd) = w;
             }
           }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      constexpr int kRowChunks = DM::CH;                        // 16-byte chunks per row of O
+      constexpr int kIt = (C::KL * kRowChunks + 63) / 64;
+#pragma unroll
+      for (int it = 0; it < kIt; ++it) {
+        const int c = it * 64 + lane;
+        const int row = c / kRowChunks, ch = c - row * kRowChunks;
+        if (row < L) {
+          const uint4 w = *reinterpret_cast<const uint4 *>(Vs + row * D + ch * 8);
+          *reinterpret_cast<uint4 *>(op + (int64_t)row * rs + ch * 8) = w;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        f32x16 oacc[DM::DT];
+#pragma unroll
+        for (int dt = 0; dt < DM::DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt)
+#pragma unroll
+          for (int ks2 = 0; ks2 < 2; ++ks2) {
+            const u16 *vb = Vs + (mt * 32 + ks2 * 16) * D + v_off;
+#pragma unroll
+            for (int dt = 0; dt < DM::DT; ++dt) {
+              uint4 u = tr_read_pair<D>(vb + dt * 32);
+              if (DM::DV != D && dt == DM::DT - 1 && !vkeep) u = make_uint4(vconst, vconst, vconst, vconst);
+              oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u), pf[nt][mt][ks2], oacc[dt],
+                                                                 0, 0, 0);
+            }
+          }
+        float l;
+        if constexpr (DM::ONES) {
+          l = __shfl(oacc[DM::ONES_DT][DM::ONES_R], l32);
+        } else {
+          l = lsum[nt];
+        }
+        const float inv = 1.0f / l;
+        const int qi = nt * 32 + l32;
+        if (qi < L) {
+          u16 *orow = op + (int64_t)qi * rs;
+#pragma unroll
+          for (int dt = 0; dt < DM::DT; ++dt)
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+              const int dd = dt * 32 + rb * 8 + g * 4;
+              if (dd + 4 <= D) {
+                uint2 w;
+                w.x = pack_bf16x2(oacc[dt][rb * 4 + 0] * inv, oacc[dt][rb * 4 + 1] * inv);
+                w.y = pack_bf16x2(oacc[dt][rb * 4 + 2] * inv, oacc[dt][rb * 4 + 3] * inv);
+                *reinterpret_cast<uint2 *>(orow + dd) = w;
+              }
+            }
+        }
       }
     }
     // the next head overwrites V: all lanes' reads of this head are done
