@@ -555,6 +555,23 @@ __global__ void __launch_bounds__(64 * kLongWaves, 8 / kLongWaves) attn_long_ker
   __syncthreads();
   if (ntl > 1) dma.issue(lds + C::STAGE, C::KB, kp, vp, rs, Lk, lane, wave);
 
+  // A wave whose queries all lie past L (the last query block of a sequence
+  // whose length is not a multiple of the block) computes nothing: it only
+  // issues its share of every tile's loads and meets the same barriers as
+  // the key loop below, then leaves.
+  if (__builtin_amdgcn_readfirstlane(q0) >= L) {
+    for (int p = 0; 2 * p + 2 < nu; ++p) {
+      const int u = 2 * p;
+      if (u % UPT == 0) {
+        const int kt = u / UPT;
+        wait_vmem();
+        __syncthreads();
+        if (kt + 2 < ntl) dma.issue(lds + ((kt + 2) % C::NSTAGE) * C::STAGE, (kt + 2) * C::KB, kp, vp, rs, Lk, lane, wave);
+      }
+    }
+    return;
+  }
+
   // K (and, + REGION, V) rows of unit u
   auto unit_rows = [&](int u) { return lds + ((u / UPT) % C::NSTAGE) * C::STAGE + (u % UPT) * 32 * D; };
   f32x16 sb[2][NT];

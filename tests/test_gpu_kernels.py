@@ -272,6 +272,7 @@ SPATIAL_CASES = [
     (2, 1, 1000, 1, 72, 3.0, BF),      # peaked softmax
     (1, 1, 1, 3, 72, 1.0, BF),         # L = 1
     (1, 3, 64, 2, 72, 1.0, BF),
+    (1, 1, 3600, 1, 72, 1.0, BF),      # 720p frame: the last 512-query block holds 16 queries, 7 waves idle
     (1, 1, 700, 3, 128, 1.0, BF),
     (1, 2, 257, 2, 64, 2.0, BF),
     (1, 2, 64, 2, 64, 1.0, F32),
