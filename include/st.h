@@ -36,6 +36,12 @@
  *     for st_relayout, which needs element alignment only.
  *   - Calls are reentrant; concurrent calls on different streams are safe as
  *     long as their output buffers and workspaces do not overlap.
+ *   - Sizes: activations may exceed 2^31 elements (every activation offset is
+ *     64-bit).  ST_EUNSUPPORTED marks the index ranges the kernels do not
+ *     cover: a weight matrix (3*H*d x c_in, n_out x k_in, c_out x H*d) of 2^31
+ *     elements or more, 2^40 rows or sequences or more, a sequence length of
+ *     2^30 or more, B*T*S of 2^31 or more in st_block_sliced*, a RoPE table of
+ *     2^31 floats or more, and st_relayout copies of 2^32 vectors or more.
  */
 #ifndef ST_H
 #define ST_H
