@@ -31,9 +31,12 @@
  *     their arguments on the host, enqueue kernels on the stream and return;
  *     they never synchronise.  Device faults surface at the caller's sync.
  *   - Errors are return codes only.  Argument validation happens before any
- *     HIP call, so an invalid call has no side effect.  Outputs must not alias
- *     inputs (ST_EINVAL).  Pointers must be 16-byte aligned (ST_EALIGN) except
- *     for st_relayout, which needs element alignment only.
+ *     HIP call, so an invalid call has no side effect.  A valid call with work
+ *     to do then checks the current device: the kernels are built for gfx950,
+ *     and any other device gives ST_EUNSUPPORTED before anything is enqueued.
+ *     Outputs must not alias inputs (ST_EINVAL).  Pointers must be 16-byte
+ *     aligned (ST_EALIGN) except for st_relayout, which needs element
+ *     alignment only.
  *   - Calls are reentrant; concurrent calls on different streams are safe as
  *     long as their output buffers and workspaces do not overlap.
  *   - Sizes: activations may exceed 2^31 elements (every activation offset is

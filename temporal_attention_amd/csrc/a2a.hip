@@ -64,6 +64,7 @@ st_status a2a_common(const void *src, void *dst, int dir, int B, int T, int S, i
   const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst, len = (uintptr_t)n * elem_bytes;
   if (a < b + len && b < a + len) return ST_EINVAL;
   const A2AMap m = a2a_map(dir, pack, B, T, S, C, P);
+  if (const st_status dc = device_ok(); dc != ST_OK) return dc;
   return pack ? launch_relayout(src, m.side, dst, m.chunk, m.dims, 5, elem_bytes, s)
               : launch_relayout(src, m.chunk, dst, m.side, m.dims, 5, elem_bytes, s);
 }

@@ -263,6 +263,7 @@ st_status block_sliced(const void *x, int B, int T, int t_valid, int S, int grid
   const int64_t N = (int64_t)B * T * S;
   const Range rx = rng(x, N * C * e), ry = rng(y, N * C * e), rw = rng(ws, (int64_t)P.total);
   if (overlap(rx, ry) || overlap(ry, rw) || overlap(rx, rw)) return ST_EINVAL;
+  if (const st_status dc = device_ok(); dc != ST_OK) return dc;
 
   char *W = static_cast<char *>(ws);
   float *rope2 = reinterpret_cast<float *>(W + P.rope2);
@@ -439,6 +440,7 @@ st_status st_rope_table(int d, int kind, float base, int n_pos, float *table, vo
   if (n_pos < 1 || !(base > 0.f) || !isfinite(base) || !table) return ST_EINVAL;
   if (!aligned16(table)) return ST_EALIGN;
   if ((int64_t)n_pos * d >= (1ll << 31)) return ST_EUNSUPPORTED;
+  if (const st_status dc = device_ok(); dc != ST_OK) return dc;
   return launch_rope_table(d, kind, (double)base, n_pos, table, (hipStream_t)stream);
 }
 
@@ -472,6 +474,8 @@ st_status st_qkv_norm_rope(const void *x, int64_t rows, int c_in, const void *w_
     for (Range out : {rq, rk, rv})
       if (overlap(out, rng(p, rows * 8))) return ST_EINVAL;
   RopeArgs ra{rope_kind, rope_npos, rope_table, pos_period, pos_offset, grid_w, p};
+  if (rows == 0) return ST_OK;
+  if (const st_status dc = device_ok(); dc != ST_OK) return dc;
   return do_qkv(x, rows, c_in, w_qkv, g_q, g_k, eps, q_scale, ra, H, d, dtype, q, k, v, (hipStream_t)stream);
 }
 
@@ -485,6 +489,8 @@ st_status st_out_proj(const void *a, int64_t rows, int k_in, const void *w, int 
   const size_t e = esize(dtype);
   const Range ry = rng(y, rows * n_out * e);
   if (overlap(ry, rng(a, rows * k_in * e)) || overlap(ry, rng(w, (int64_t)n_out * k_in * e))) return ST_EINVAL;
+  if (rows == 0) return ST_OK;
+  if (const st_status dc = device_ok(); dc != ST_OK) return dc;
   return do_linear(a, rows, k_in, w, n_out, dtype, y, (hipStream_t)stream);
 }
 
@@ -499,6 +505,8 @@ st_status st_out_proj_relayout(const void *a, int64_t rows, int k_in, const void
   const size_t e = esize(dtype);
   const Range ry = rng(y, rows * n_out * e);
   if (overlap(ry, rng(a, rows * k_in * e)) || overlap(ry, rng(w, (int64_t)n_out * k_in * e))) return ST_EINVAL;
+  if (rows == 0) return ST_OK;
+  if (const st_status dc = device_ok(); dc != ST_OK) return dc;
   return do_linear(a, rows, k_in, w, n_out, dtype, y, (hipStream_t)stream, row_swap(n1, n2));
 }
 
@@ -527,13 +535,18 @@ static st_status attn_common(const void *q, const void *k, const void *v, int64_
   const Range ro = rng(out, w_o ? rows * c_out * e : bytes);
   if (overlap(ro, rq) || overlap(ro, rk) || overlap(ro, rv)) return ST_EINVAL;
   hipStream_t s = (hipStream_t)stream;
-  if (!w_o) return do_attn(q, k, v, outer, L, nv, H, d, scale, dtype, out, temporal, s);
+  if (rows == 0) return ST_OK;
+  if (!w_o) {
+    if (const st_status dc = device_ok(); dc != ST_OK) return dc;
+    return do_attn(q, k, v, outer, L, nv, H, d, scale, dtype, out, temporal, s);
+  }
   if (!ws || ws_bytes < st_attn_workspace(rows, H, d, dtype)) return ST_EWORKSPACE;
   if (!aligned16(w_o) || !aligned16(ws)) return ST_EALIGN;
   const Range rw = rng(w_o, (int64_t)c_out * H * d * e), rs = rng(ws, bytes);
   if (overlap(ro, rw) || overlap(ro, rs)) return ST_EINVAL;
   for (const Range &in : {rq, rk, rv, rw})
     if (overlap(rs, in)) return ST_EINVAL;
+  if (const st_status dc = device_ok(); dc != ST_OK) return dc;
   const st_status r = do_attn(q, k, v, outer, L, nv, H, d, scale, dtype, ws, temporal, s);
   if (r != ST_OK) return r;
   return do_linear(ws, rows, H * d, w_o, c_out, dtype, out, s);
@@ -581,6 +594,7 @@ st_status st_attn_chunk(const void *q, const void *k, const void *v, int64_t out
   if (outer == 0 || Lq == 0) return ST_OK;
   hipStream_t s = (hipStream_t)stream;
   const int e = (int)esize(dtype);
+  if (const st_status dc = device_ok(); dc != ST_OK) return dc;
   if (kv_valid == 0) return launch_attn_empty(out, lse, outer, Lq, H, d, e, s);
   if (dtype == ST_F32)
     return launch_attn_chunk_f32((const float *)q, (const float *)k, (const float *)v, outer, Lq, Lk, kv_valid, H, d,
@@ -593,6 +607,7 @@ st_status st_attn_chunk_acc(const void *q, const void *k, const void *v, int64_t
   const st_status c = chunk_check(q, k, v, outer, Lq, Lk, kv_valid, H, d, scale, dtype, acc_o, acc_lse);
   if (c != ST_OK) return c;
   if (outer == 0 || Lq == 0 || kv_valid == 0) return ST_OK;   // an empty chunk leaves the accumulator as it is
+  if (const st_status dc = device_ok(); dc != ST_OK) return dc;
   hipStream_t s = (hipStream_t)stream;
   if (dtype == ST_F32)
     return launch_attn_chunk_f32((const float *)q, (const float *)k, (const float *)v, outer, Lq, Lk, kv_valid, H, d,
@@ -618,6 +633,7 @@ st_status st_attn_merge(const void *o_a, const float *lse_a, const void *o_b, co
   for (const Range &x : {rl, rla, rlb})
     if (overlap(ro, x) || overlap(ra, x) || overlap(rb, x)) return ST_EINVAL;
   if (outer == 0 || L == 0) return ST_OK;
+  if (const st_status dc = device_ok(); dc != ST_OK) return dc;
   return launch_attn_merge(o_a, lse_a, o_b, lse_b, outer, L, H, d, (int)esize(dtype), out, lse, (hipStream_t)stream);
 }
 
@@ -638,6 +654,7 @@ st_status st_v_change(const void *v_new, void *v_cache, int64_t rows, int H, int
   for (const Range &o : {rm, ri, rk})
     if (overlap(o, rn) || overlap(o, rc)) return ST_EINVAL;
   if (overlap(rm, ri) || overlap(rm, rk) || overlap(ri, rk)) return ST_EINVAL;
+  if (const st_status dc = device_ok(); dc != ST_OK) return dc;
   return launch_v_change(v_new, v_cache, nvec, d, (int)e, threshold, mask, active_idx, n_active, update_cache,
                          (hipStream_t)stream);
 }
@@ -662,6 +679,7 @@ st_status st_relayout(const void *src, const int64_t *src_strides, void *dst, co
   const Range rs{(uintptr_t)src + smin * elem_bytes, (uintptr_t)src + (smax + 1) * elem_bytes};
   const Range rd{(uintptr_t)dst + dmin * elem_bytes, (uintptr_t)dst + (dmax + 1) * elem_bytes};
   if (overlap(rs, rd)) return ST_EINVAL;
+  if (const st_status dc = device_ok(); dc != ST_OK) return dc;
   return launch_relayout(src, src_strides, dst, dst_strides, dims, ndim, elem_bytes, (hipStream_t)stream);
 }
 
@@ -715,6 +733,7 @@ st_status st_block_sliced_noalloc(const void *x, int B, int T, int t_valid, int 
   if (c != ST_OK) return c;
   const size_t need = st_block_sliced_workspace(B, T, S, grid_w, C, H, d, n_t, n_s, dtype);
   if (need == 0 || need > kScratchBytes) return ST_EWORKSPACE;
+  if (const st_status dc = device_ok(); dc != ST_OK) return dc;
   void *ws = nullptr;
   const st_status r = scratch_for_current_device(&ws);
   if (r != ST_OK) return r;

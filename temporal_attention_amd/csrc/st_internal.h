@@ -3,6 +3,9 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <string.h>
+
+#include <atomic>
 
 #include "../../include/st.h"
 
@@ -40,6 +43,25 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t bid, uint32_t nblocks) {
 }
 
 inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// The kernels are compiled for gfx950 only.  Every call that launches work
+// checks the current device after its argument checks (cached per device) and
+// refuses any other architecture with ST_EUNSUPPORTED rather than failing at
+// the launch.
+inline st_status device_ok() {
+  static std::atomic<int> arch[64];   // 0 not looked up, 1 gfx950, 2 another architecture
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return ST_ELAUNCH;
+  int a = dev < 64 ? arch[dev].load(std::memory_order_relaxed) : 0;
+  if (a == 0) {
+    hipDeviceProp_t p;
+    if (hipGetDeviceProperties(&p, dev) != hipSuccess) return ST_ELAUNCH;
+    const char *n = p.gcnArchName;   // e.g. "gfx950:sramecc+:xnack-"
+    a = (strncmp(n, "gfx950", 6) == 0 && (n[6] == '\0' || n[6] == ':')) ? 1 : 2;
+    if (dev < 64) arch[dev].store(a, std::memory_order_relaxed);
+  }
+  return a == 1 ? ST_OK : ST_EUNSUPPORTED;
+}
 
 inline st_status launch_status() {
   return hipGetLastError() == hipSuccess ? ST_OK : ST_ELAUNCH;
