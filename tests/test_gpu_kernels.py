@@ -215,6 +215,33 @@ def test_qkv_zero_rows_is_noop():
     assert bool((q.float() == 3.0).all())
 
 
+def test_empty_calls_return_ok_and_write_nothing():
+    """Zero sequences, zero-length sequences and zero rows: every call returns ST_OK (the binding
+    raises otherwise) and leaves a sentinel-filled output untouched; V-Major reports 0 active."""
+    H, d, C = 16, 72, 1152
+    src = empty((64, H, d))
+    w = empty((C, H * d))
+    out = empty((64, C))
+    out.fill_(5.0)
+    ws = t_.empty(1 << 20, dtype=t_.uint8, device="cuda")
+    for B, T, S in ((0, 3, 100), (1, 0, 100), (1, 3, 0)):
+        st.st_attn_spatial(src, src, src, B, T, S, H, d, 0.1, BF, None, 0, out)
+        st.st_attn_spatial(src, src, src, B, T, S, H, d, 0.1, BF, w, C, out, ws, ws.numel())
+        st.st_attn_temporal(src, src, src, B, S, T, T, H, d, 0.1, BF, None, 0, out)
+    st.st_out_proj(src, 0, H * d, w, C, BF, out)
+    st.st_out_proj_relayout(src, 0, H * d, w, C, BF, 4, 5, out)
+    lse = t_.full((64,), 7.0, device="cuda")
+    st.st_attn_chunk(src, src, src, 1, 0, 50, 50, H, d, 0.1, BF, out, lse)
+    st.st_attn_merge(src, lse, src, lse, 0, 50, H, d, BF, out, lse)
+    mask = t_.full((64,), 9, dtype=t_.uint8, device="cuda")
+    cnt = t_.full((1,), 123, dtype=t_.int64, device="cuda")
+    st.st_v_change(src, empty((64, H, d)), 0, H, d, 1.0, BF, mask, None, cnt, 1)
+    sync()
+    assert bool((out.float() == 5.0).all())
+    assert bool((lse == 7.0).all()) and bool((mask == 9).all())
+    assert int(cnt.item()) == 0
+
+
 # --------------------------------------------------------------------------- #
 # Output projection                                                            #
 # --------------------------------------------------------------------------- #
