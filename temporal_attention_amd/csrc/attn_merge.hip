@@ -6,12 +6,15 @@
 // scaled scores; the union's output weights each part by exp(lse_part -
 // lse_union).
 //
-// Rows (one per (sequence, query, head)) that start 16-byte aligned and have
-// at most 64 16-byte pieces take the contiguous-pass kernel: a wavefront pass
-// covers floor(64 / pieces) consecutive rows as one contiguous run.  Other
-// rows take a group of LPR lanes per row.  In both, a row never straddles
-// wavefronts and every lane issues its reads of both parts before any write,
-// so the merge may run in place on either input.
+// Rows (one per (sequence, query, head)) that start 16-byte aligned take the
+// blocked kernel: a workgroup takes 32 consecutive queries with all their
+// heads (one contiguous run of rows), computes their weights once, reading
+// and writing each head's log-sum-exps as one run of 32 floats, then streams
+// the rows 16 bytes per thread.  With more than 256 heads such rows take the
+// contiguous-pass kernel (a wavefront pass covers floor(64 / pieces)
+// consecutive rows); other rows take a group of LPR lanes per row.  In all of
+// them every element is read and written by one thread, reads first, so the
+// merge may run in place on either input.
 // HBM-bound: per row, two rows and two log-sum-exps in, one of each out.
 #include <math.h>
 
@@ -130,6 +133,63 @@ __global__ void __launch_bounds__(256) attn_merge_flat_kernel(const T *oa, const
   }
 }
 
+// Blocks of 32 consecutive query rows (ql = outer * L + query) with all H
+// heads: rows r = ql * H + h, contiguous in o.  The 32 * H merge weights are
+// computed first, one thread per (h, query), so a block reads and writes each
+// head's log-sum-exps as one run of 32 floats; then every thread streams
+// 16-byte pieces of the block's rows, U pieces loaded before any is stored (a
+// piece is read and written by the same thread, so this holds in place too).
+template <typename T, int U>
+__global__ void __launch_bounds__(256) attn_merge_blk_kernel(const T *oa, const float *la, const T *ob,
+                                                             const float *lb, int64_t nql, int L, int H, int P, T *o,
+                                                             float *lse) {
+  constexpr int VW = 16 / sizeof(T);            // elements per 16-byte piece
+  extern __shared__ float wgt[];                // [2][32 * H]: fa, fb per row of the block
+  const int64_t ql0 = (int64_t)blockIdx.x * 32;
+  const int nq = (int)min<int64_t>(32, nql - ql0);
+  for (int t = threadIdx.x; t < 32 * H; t += blockDim.x) {
+    const int h = t >> 5, qo = t & 31;
+    if (qo >= nq) continue;
+    const int64_t ql = ql0 + qo;
+    const int64_t li = (ql / L * H + h) * L + ql % L;
+    const float a = la[li], b = lb[li];
+    const float m = fmaxf(a, b);
+    const bool empty = m == -INFINITY;          // neither part has a valid key
+    const float wa = empty ? 0.f : expf(a - m), wb = empty ? 0.f : expf(b - m);
+    const float tot = wa + wb;
+    wgt[qo * H + h] = empty ? 0.f : wa / tot;
+    wgt[32 * H + qo * H + h] = empty ? 0.f : wb / tot;
+    lse[li] = empty ? -INFINITY : m + logf(tot);
+  }
+  __syncthreads();
+  const int nv = nq * H * P;                    // pieces of the block's rows
+  const int64_t v0 = ql0 * H * P;
+  const float invp = 1.0f / (float)P;
+  for (int vb = 0; vb < nv; vb += U * (int)blockDim.x) {
+    uint4 x[U], y[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int v = vb + u * (int)blockDim.x + (int)threadIdx.x;
+      if (v < nv) {
+        x[u] = *reinterpret_cast<const uint4 *>(oa + (v0 + v) * VW);
+        y[u] = *reinterpret_cast<const uint4 *>(ob + (v0 + v) * VW);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int v = vb + u * (int)blockDim.x + (int)threadIdx.x;
+      if (v >= nv) continue;
+      int rr = (int)(((float)v + 0.5f) * invp);   // row within the block (v < 2^22: exact)
+      const float fa = wgt[rr], fb = wgt[32 * H + rr];
+      const T *xe = reinterpret_cast<const T *>(&x[u]), *ye = reinterpret_cast<const T *>(&y[u]);
+      T z[VW];
+#pragma unroll
+      for (int e = 0; e < VW; ++e) z[e] = Elem<T>::store(fmaf(fa, Elem<T>::load(xe[e]), fb * Elem<T>::load(ye[e])));
+      *reinterpret_cast<uint4 *>(o + (v0 + v) * VW) = *reinterpret_cast<const uint4 *>(z);
+    }
+  }
+}
+
 template <typename T>
 __global__ void __launch_bounds__(256) attn_empty_kernel(T *o, float *lse, int64_t n_o, int64_t n_lse) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -169,6 +229,22 @@ st_status launch_attn_merge(const void *o_a, const float *lse_a, const void *o_b
   const int64_t rows = outer * L * H;
   if (rows == 0) return ST_OK;
   const int pieces = d * elem_bytes / 16;
+  if ((d * elem_bytes) % 16 == 0 && H <= 256) {   // blocks of 32 queries x H heads
+    const int64_t nql = outer * L;
+    const int64_t blocks = (nql + 31) / 32;
+    const size_t shm = (size_t)2 * 32 * H * sizeof(float);
+    if (blocks < (1ll << 31)) {
+      if (elem_bytes == 2)
+        hipLaunchKernelGGL((attn_merge_blk_kernel<u16, 4>), dim3((uint32_t)blocks), dim3(256), shm, s,
+                           static_cast<const u16 *>(o_a), lse_a, static_cast<const u16 *>(o_b), lse_b, nql, L, H,
+                           pieces, static_cast<u16 *>(o), lse);
+      else
+        hipLaunchKernelGGL((attn_merge_blk_kernel<float, 4>), dim3((uint32_t)blocks), dim3(256), shm, s,
+                           static_cast<const float *>(o_a), lse_a, static_cast<const float *>(o_b), lse_b, nql, L, H,
+                           pieces, static_cast<float *>(o), lse);
+      return launch_status();
+    }
+  }
   if ((d * elem_bytes) % 16 == 0 && pieces <= 64) {
     if (elem_bytes == 2) merge_flat_launch<u16>(o_a, lse_a, o_b, lse_b, rows, L, H, pieces, o, lse, s);
     else merge_flat_launch<float>(o_a, lse_a, o_b, lse_b, rows, L, H, pieces, o, lse, s);
